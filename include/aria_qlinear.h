@@ -1,0 +1,146 @@
+/*
+ * aria_qlinear.h — C-ABI of the quantized linear layer ("qlinear") of a
+ * diffusion-transformer denoising step, for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes follows the aria pages ("A Quantized Native Runtime for
+ * On-Device Semantic Audio Generation"):
+ *   - project page, "What aria is", bullet "Quantization that saves memory":
+ *     transformer weights are packed once from fp16 down to 8 or 4 bits and the
+ *     fp16 copy is released, so the packed form replaces the footprint;
+ *   - project page, "Results", table "Quantization is close to free at 8-bit":
+ *     three precisions of the linear layers — q8 (8-bit weights, fp16
+ *     activations; here W8A16), W8A8 (8-bit arithmetic on integer matrix
+ *     units; here int8 x int8 -> int32) and q4 (4-bit weights; here W4A16).
+ *     q8 and W8A8 have the same memory, so both read ONE stored int8 format;
+ *   - project page, "Results", "Steering is real, inside a narrow window" and
+ *     "Live steering while streaming": a direction d is added with strength
+ *     alpha to one block's residual stream, alpha = 0 removes it with
+ *     bit-identical output, and alpha lives inside a captured graph (so it is
+ *     read from device memory here).
+ * The pages do not give the formulas; the library uses these readings:
+ *   scale s = fp16_RNE(max|v| / qmax), q = clamp(RNE(v / s), -qmax, qmax);
+ *   qmax 127 for 8 bits, 7 for 4 bits; weights per output channel (8-bit) or
+ *   per (output channel, group of 32 consecutive k) (4-bit); activations per
+ *   token (row); s == 0 gives q == 0; every scale is stored as fp16;
+ *   epilogue order: dequantize -> + bias -> GELU(tanh) -> + residual -> + alpha*d.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE memory owned by the caller unless stated otherwise.
+ *     The library allocates nothing and keeps no state between calls.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = null stream);
+ *     they never synchronise and never read device memory on the host, so they
+ *     may be captured into a HIP graph.
+ *   - All argument checks run on the host before anything is launched; on an
+ *     error nothing is launched and a negative aria_status is returned.  A
+ *     failed launch returns ARIA_E_HIP.  Errors inside a kernel surface at the
+ *     caller's next synchronisation.  Inputs must be finite.
+ *   - Shapes: M tokens, K inputs, N outputs; M, N >= 1, K >= 32 and
+ *     K % 32 == 0.  Every pointer must be 16-byte aligned.
+ *   - Layouts (row-major):
+ *       X   fp16 [M][K]            activations
+ *       W   fp16 [K][N]            unpacked weights (input of aria_qpack only)
+ *       Wq  int8 [N][K]            8-bit weights, row n contiguous along K
+ *       s_w fp16 [N]               8-bit weight scales
+ *       Wq4 uint8 [N][K/2]         4-bit weights: byte j of row n holds
+ *                                  k = 2j in its low nibble, k = 2j+1 in its
+ *                                  high nibble, two's complement
+ *       s_g fp16 [N][K/32]         4-bit group scales, group g = k in [32g, 32g+32)
+ *       Y   fp16 [M][N]            output
+ */
+#ifndef ARIA_QLINEAR_H
+#define ARIA_QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* aria_stream_t; /* a hipStream_t */
+
+enum aria_status {
+    ARIA_OK = 0,
+    ARIA_E_NULL = -1,        /* a required pointer is NULL                         */
+    ARIA_E_SHAPE = -2,       /* M, K or N out of range, or K % 32 != 0             */
+    ARIA_E_ALIGN = -3,       /* a pointer is not 16-byte aligned                   */
+    ARIA_E_UNSUPPORTED = -4, /* bits not in {4, 8}, or group not 0 (8-bit) / 32 (4-bit) */
+    ARIA_E_WORKSPACE = -5,   /* workspace missing or smaller than required         */
+    ARIA_E_HIP = -6,         /* the HIP runtime reported an error at launch        */
+    ARIA_E_ALIAS = -7        /* x overlaps y                                       */
+};
+
+enum aria_mode { ARIA_W8A8 = 0, ARIA_W8A16 = 1, ARIA_W4A16 = 2 };
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* aria_status_string(int status);
+
+/* Library ABI version (increments on incompatible change). */
+int aria_abi_version(void);
+
+/* Host-only: bytes of the packed weights and of their scales.
+ *   bits 8, group 0 : q = K*N, s = 2*N
+ *   bits 4, group 32: q = K*N/2, s = 2*N*(K/32)
+ * q_bytes / s_bytes are host pointers. */
+int aria_qpack_bytes(int bits, int group, int64_t K, int64_t N, size_t* q_bytes, size_t* s_bytes);
+
+/* a1 — pack fp16 weights W [K][N] (project page, "What aria is": weights from
+ * fp16 down to 8 or 4 bits).  bits 8 / group 0 -> Wq int8 [N][K] + s_w fp16 [N];
+ * bits 4 / group 32 -> Wq4 uint8 [N][K/2] + s_g fp16 [N][K/32].  q_out and
+ * s_out must hold aria_qpack_bytes() bytes.  Once the call has completed on the
+ * stream the caller may free W: nothing later reads it. */
+int aria_qpack(int bits, int group, const void* w_f16, int64_t K, int64_t N,
+               void* q_out, void* s_out, aria_stream_t stream);
+
+/* a2 — per-token dynamic activation quantization used by W8A8 (project page,
+ * "Results": W8A8 runs 8-bit arithmetic, so activations become int8 too):
+ * X fp16 [M][K] -> Xq int8 [M][K] + s_a fp16 [M].  Exposed for testing and for
+ * callers that quantize once and reuse. */
+int aria_quant_act(const void* x_f16, int64_t M, int64_t K, int8_t* xq, void* s_a_f16,
+                   aria_stream_t stream);
+
+/* a5 — epilogue applied to every output element y[m][n] (in fp32, then
+ * rounded to fp16 once): dequantize, then each optional term in this order. */
+typedef struct aria_epilogue {
+    const void* bias;         /* fp16 [N] or NULL                                        */
+    int32_t gelu;             /* 0 none, 1 GELU tanh form:
+                                 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))        */
+    int32_t reserved;         /* must be 0                                               */
+    const void* residual;     /* fp16 [M][N] or NULL; may be the same buffer as y        */
+    const float* steer_dir;   /* fp32 [N] or NULL: steering direction d                  */
+    const float* steer_alpha; /* DEVICE fp32 scalar alpha, or NULL; read by the kernel at
+                                 run time (graph-updatable); alpha == 0 skips the term   */
+    int32_t* acc_out;         /* W8A8 only, optional: the raw int32 accumulators [M][N]  */
+} aria_epilogue;
+
+/* Workspace (device bytes) the qlinear call needs for this shape; 0 = none.
+ * W8A8 needs room for Xq int8 [M][K] and s_a fp16 [M]; the weight-only modes
+ * need room for split-K partial sums at small M. */
+size_t aria_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, int64_t N);
+
+/* a2+a4+a5 — W8A8: Y = epilogue( (sum_k Xq[m][k] * Wq[n][k]) * s_a[m] * s_w[n] )
+ * with Xq, s_a the per-token quantization of X (written to the workspace) and
+ * an exact int32 accumulator.  epi may be NULL (plain output).  x must not
+ * overlap y. */
+int aria_qlinear_w8a8(const void* x_f16, int64_t M, int64_t K, int64_t N,
+                      const int8_t* wq, const void* s_w_f16, const aria_epilogue* epi,
+                      void* y_f16, void* ws, size_t ws_bytes, aria_stream_t stream);
+
+/* a3+a4+a5 — W8A16 (the pages' q8): Y = epilogue( s_w[n] * sum_k X[m][k] * Wq[n][k] )
+ * with fp32 accumulation.  Reads the same Wq / s_w as W8A8. */
+int aria_qlinear_w8a16(const void* x_f16, int64_t M, int64_t K, int64_t N,
+                       const int8_t* wq, const void* s_w_f16, const aria_epilogue* epi,
+                       void* y_f16, void* ws, size_t ws_bytes, aria_stream_t stream);
+
+/* a3+a4+a5 — W4A16 (the pages' q4):
+ * Y = epilogue( sum_k X[m][k] * fp16(q4[n][k] * s_g[n][k/32]) ) with fp32
+ * accumulation; group must be 32. */
+int aria_qlinear_w4a16(const void* x_f16, int64_t M, int64_t K, int64_t N,
+                       const uint8_t* wq4, const void* s_g_f16, int group,
+                       const aria_epilogue* epi, void* y_f16, void* ws, size_t ws_bytes,
+                       aria_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ARIA_QLINEAR_H */

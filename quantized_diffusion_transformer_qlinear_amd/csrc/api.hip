@@ -1,0 +1,179 @@
+// The C-ABI of the qlinear library (declared in include/aria_qlinear.h).
+// Host-side only: validates every argument before anything is launched, lays
+// out the caller's workspace, and enqueues the kernels on the caller's stream.
+// No allocation, no synchronisation, no device reads on the host.
+#include "../../include/aria_qlinear.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace aria;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // M and N limits (int indexing in kernels)
+constexpr int64_t kMaxK = 16384;                 // activation-quant keeps a row in registers
+constexpr size_t kAlign = 256;                    // workspace sub-buffer alignment
+
+inline bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_shape(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || N < 1 || K < 32 || (K % 32) != 0) return ARIA_E_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxK) return ARIA_E_SHAPE;
+    if (M * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40)) return ARIA_E_SHAPE;
+    return ARIA_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Validate the epilogue and convert it to the kernels' form.
+int make_epi(const aria_epilogue* e, int mode, int64_t M, int64_t N, const void* y, Epi* out) {
+    *out = Epi{nullptr, nullptr, nullptr, nullptr, nullptr, 0};
+    if (!e) return ARIA_OK;
+    if (e->reserved != 0 || (e->gelu != 0 && e->gelu != 1)) return ARIA_E_UNSUPPORTED;
+    if (e->acc_out && mode != ARIA_W8A8) return ARIA_E_UNSUPPORTED;
+    if (e->steer_dir && !e->steer_alpha) return ARIA_E_NULL;
+    if (!aligned16(e->bias) || !aligned16(e->residual) || !aligned16(e->steer_dir) ||
+        !aligned16(e->steer_alpha) || !aligned16(e->acc_out))
+        return ARIA_E_ALIGN;
+    // the residual may be exactly y (in-place h += ...), but must not partly overlap it
+    const size_t ybytes = (size_t)(M * N) * 2;
+    if (e->residual && e->residual != y && overlap(e->residual, ybytes, y, ybytes)) return ARIA_E_ALIAS;
+    out->bias = static_cast<const half_t*>(e->bias);
+    out->residual = static_cast<const half_t*>(e->residual);
+    out->steer_dir = e->steer_dir;
+    out->steer_alpha = e->steer_dir ? e->steer_alpha : nullptr;
+    out->acc_out = e->acc_out;
+    out->gelu = e->gelu;
+    return ARIA_OK;
+}
+
+size_t w8a8_ws(int64_t M, int64_t K) { return round_up((size_t)(M * K), kAlign) + round_up((size_t)M * 2, kAlign); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ARIA_OK : ARIA_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* aria_status_string(int s) {
+    switch (s) {
+        case ARIA_OK: return "ok";
+        case ARIA_E_NULL: return "a required pointer is NULL";
+        case ARIA_E_SHAPE: return "M, K or N out of range (M, N >= 1; 32 <= K <= 16384; K % 32 == 0)";
+        case ARIA_E_ALIGN: return "a pointer is not 16-byte aligned";
+        case ARIA_E_UNSUPPORTED: return "unsupported bits/group/epilogue option";
+        case ARIA_E_WORKSPACE: return "workspace missing or too small";
+        case ARIA_E_HIP: return "HIP runtime error at launch";
+        case ARIA_E_ALIAS: return "output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+int aria_abi_version(void) { return 1; }
+
+int aria_qpack_bytes(int bits, int group, int64_t K, int64_t N, size_t* q_bytes, size_t* s_bytes) {
+    if (!q_bytes || !s_bytes) return ARIA_E_NULL;
+    if (check_shape(1, K, N) != ARIA_OK) return ARIA_E_SHAPE;
+    if (bits == 8 && group == 0) {
+        *q_bytes = (size_t)(K * N);
+        *s_bytes = (size_t)N * 2;
+        return ARIA_OK;
+    }
+    if (bits == 4 && group == 32) {
+        *q_bytes = (size_t)(K * N) / 2;
+        *s_bytes = (size_t)N * (size_t)(K / 32) * 2;
+        return ARIA_OK;
+    }
+    return ARIA_E_UNSUPPORTED;
+}
+
+int aria_qpack(int bits, int group, const void* w, int64_t K, int64_t N, void* q, void* s,
+               aria_stream_t stream) {
+    size_t qb, sb;
+    const int rc = aria_qpack_bytes(bits, group, K, N, &qb, &sb);
+    if (rc != ARIA_OK) return rc;
+    if (!w || !q || !s) return ARIA_E_NULL;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return ARIA_E_ALIGN;
+    if (overlap(w, (size_t)(K * N) * 2, q, qb) || overlap(w, (size_t)(K * N) * 2, s, sb)) return ARIA_E_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const half_t* wh = static_cast<const half_t*>(w);
+    if (bits == 8) return hip_status(launch_qpack8(wh, K, N, static_cast<int8_t*>(q), static_cast<half_t*>(s), st));
+    return hip_status(launch_qpack4(wh, K, N, static_cast<uint8_t*>(q), static_cast<half_t*>(s), st));
+}
+
+int aria_quant_act(const void* x, int64_t M, int64_t K, int8_t* xq, void* sa, aria_stream_t stream) {
+    if (check_shape(M, K, 1) != ARIA_OK) return ARIA_E_SHAPE;
+    if (!x || !xq || !sa) return ARIA_E_NULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(sa)) return ARIA_E_ALIGN;
+    if (overlap(x, (size_t)(M * K) * 2, xq, (size_t)(M * K))) return ARIA_E_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(launch_actquant(static_cast<const half_t*>(x), M, K, xq, static_cast<half_t*>(sa),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t aria_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, int64_t N) {
+    if (check_shape(M, K, N) != ARIA_OK) return 0;
+    switch (mode) {
+        case ARIA_W8A8: return w8a8_ws(M, K);
+        case ARIA_W8A16: return wxa16_workspace_bytes(8, M, K, N);
+        case ARIA_W4A16: return wxa16_workspace_bytes(4, M, K, N);
+        default: return 0;
+    }
+}
+
+int aria_qlinear_w8a8(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
+                      const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
+    int rc = check_shape(M, K, N);
+    if (rc != ARIA_OK) return rc;
+    if (!x || !wq || !sw || !y) return ARIA_E_NULL;
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(sw) || !aligned16(y) || !aligned16(ws)) return ARIA_E_ALIGN;
+    if (overlap(x, (size_t)(M * K) * 2, y, (size_t)(M * N) * 2)) return ARIA_E_ALIAS;
+    Epi e;
+    if ((rc = make_epi(epi, ARIA_W8A8, M, N, y, &e)) != ARIA_OK) return rc;
+    const size_t need = w8a8_ws(M, K);
+    if (!ws || ws_bytes < need) return ARIA_E_WORKSPACE;
+    int8_t* xq = static_cast<int8_t*>(ws);
+    half_t* sa = reinterpret_cast<half_t*>(static_cast<char*>(ws) + round_up((size_t)(M * K), kAlign));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if ((rc = hip_status(launch_actquant(static_cast<const half_t*>(x), M, K, xq, sa, st))) != ARIA_OK) return rc;
+    return hip_status(launch_gemm_w8a8(xq, wq, sa, static_cast<const half_t*>(sw), static_cast<half_t*>(y),
+                                       (int)M, (int)N, (int)K, e, st));
+}
+
+static int wxa16(int bits, const void* x, int64_t M, int64_t K, int64_t N, const void* wq, const void* s,
+                 const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
+    int rc = check_shape(M, K, N);
+    if (rc != ARIA_OK) return rc;
+    if (!x || !wq || !s || !y) return ARIA_E_NULL;
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(s) || !aligned16(y) || !aligned16(ws)) return ARIA_E_ALIGN;
+    if (overlap(x, (size_t)(M * K) * 2, y, (size_t)(M * N) * 2)) return ARIA_E_ALIAS;
+    Epi e;
+    if ((rc = make_epi(epi, bits == 8 ? ARIA_W8A16 : ARIA_W4A16, M, N, y, &e)) != ARIA_OK) return rc;
+    const size_t need = wxa16_workspace_bytes(bits, M, K, N);
+    if (need && (!ws || ws_bytes < need)) return ARIA_E_WORKSPACE;
+    (void)hipGetLastError();
+    return hip_status(launch_gemm_wxa16(bits, static_cast<const half_t*>(x), wq, static_cast<const half_t*>(s),
+                                        static_cast<half_t*>(y), (int)M, (int)N, (int)K, e, ws, ws_bytes,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int aria_qlinear_w8a16(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
+                       const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
+    return wxa16(8, x, M, K, N, wq, sw, epi, y, ws, ws_bytes, stream);
+}
+
+int aria_qlinear_w4a16(const void* x, int64_t M, int64_t K, int64_t N, const uint8_t* wq4, const void* sg,
+                       int group, const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes,
+                       aria_stream_t stream) {
+    if (group != 32) return ARIA_E_UNSUPPORTED;
+    return wxa16(4, x, M, K, N, wq4, sg, epi, y, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

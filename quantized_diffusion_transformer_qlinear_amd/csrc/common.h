@@ -1,0 +1,64 @@
+// Shared device helpers of the qlinear HIP library (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aria {
+
+typedef _Float16 half_t;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef uint32_t u32;
+
+constexpr int WAVE = 64;
+
+// Epilogue operands as the kernels see them (already validated on the host).
+struct Epi {
+    const half_t* bias;      // [N] or null
+    const half_t* residual;  // [M][N] or null (may alias y)
+    const float* steer_dir;  // [N] or null
+    const float* steer_alpha;  // device scalar or null
+    int32_t* acc_out;        // W8A8 raw accumulators [M][N] or null
+    int gelu;
+};
+
+// GELU, tanh form (Hendrycks & Gimpel): 0.5 y (1 + tanh(u)), u = sqrt(2/pi)(y + 0.044715 y^3).
+// Uses 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float gelu_tanh(float y) {
+    const float k2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+    float u = y + 0.044715f * y * y * y;
+    float e = __builtin_amdgcn_exp2f(k2 * u);
+    return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Steering strength, read once per thread from device memory (0 if absent).
+__device__ __forceinline__ float load_alpha(const Epi& e) {
+    return (e.steer_dir && e.steer_alpha) ? __builtin_nontemporal_load(e.steer_alpha) : 0.0f;
+}
+
+// y (the dequantized accumulator) -> + bias -> GELU -> + residual -> + alpha d.
+// `idx` is m * N + n.
+__device__ __forceinline__ float epilogue_apply(float y, int64_t idx, int n, const Epi& e,
+                                                float alpha) {
+    if (e.bias) y += (float)e.bias[n];
+    if (e.gelu) y = gelu_tanh(y);
+    if (e.residual) y += (float)e.residual[idx];
+    if (alpha != 0.0f) y += alpha * e.steer_dir[n];
+    return y;
+}
+
+// XCD-aware remap of a linear workgroup id: the hardware deals workgroups
+// round-robin over the 8 XCDs (id % 8); renumber so that consecutive logical
+// ids land on the same XCD and therefore share its L2.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+    const int NX = 8;
+    if (total % NX) return id;  // only exact multiples are remapped
+    return (id % NX) * (total / NX) + id / NX;
+}
+
+}  // namespace aria

@@ -1,0 +1,24 @@
+// Internal launcher declarations (C++ linkage; the C-ABI lives in api.hip).
+#pragma once
+
+#include "common.h"
+
+namespace aria {
+
+hipError_t launch_qpack8(const half_t* w, int64_t K, int64_t N, int8_t* q, half_t* s, hipStream_t st);
+hipError_t launch_qpack4(const half_t* w, int64_t K, int64_t N, uint8_t* q4, half_t* s, hipStream_t st);
+hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, half_t* sa, hipStream_t st);
+
+// W8A8 contraction + epilogue: A = Xq int8 [M][K], B = Wq int8 [N][K].
+hipError_t launch_gemm_w8a8(const int8_t* xq, const int8_t* wq, const half_t* sa, const half_t* sw,
+                            half_t* y, int M, int N, int K, const Epi& epi, hipStream_t st);
+
+// Weight-only contraction + epilogue: A = X fp16 [M][K]; bits 8: B = Wq int8 [N][K] with
+// per-channel scales s [N]; bits 4: B = Wq4 [N][K/2] with group scales s [N][K/32].
+// ws / ws_bytes: split-K partials for small M (may be null when not needed).
+hipError_t launch_gemm_wxa16(int bits, const half_t* x, const void* wq, const half_t* s, half_t* y,
+                             int M, int N, int K, const Epi& epi, void* ws, size_t ws_bytes,
+                             hipStream_t st);
+size_t wxa16_workspace_bytes(int bits, int64_t M, int64_t K, int64_t N);
+
+}  // namespace aria

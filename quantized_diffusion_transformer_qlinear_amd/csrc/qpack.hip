@@ -1,0 +1,134 @@
+// a1 — weight packing kernels (one-off, at load time).
+//
+// The aria project page ("What aria is", bullet "Quantization that saves
+// memory") packs the transformer weights from fp16 down to 8 or 4 bits and
+// releases the fp16 copy.  Symmetric absmax quantization with an fp16 scale:
+//   s = fp16_RNE(max|v| / qmax),  q = clamp(RNE(v / s), -qmax, qmax),  s == 0 -> q = 0
+// q8 : per output channel n over all K, qmax 127 -> Wq int8 [N][K], s [N]
+// q4 : per (n, group of 32 k), qmax 7 -> two's-complement nibbles, even k in
+//      the low nibble, Wq4 uint8 [N][K/2], s [N][K/32]
+//
+// Bit-exactness with the fp64 definition: the scale is formed as an IEEE fp32
+// quotient rounded to fp16 (equal to rounding the exact quotient, because fp32
+// carries more than twice fp16's precision), and q uses an IEEE fp32 division
+// followed by round-to-nearest-even (v_rndne_f32): the quotient of two fp16
+// values is either exactly a half-integer or at least 2^-12 (relative) away
+// from one, far beyond fp32's division error.  The library is therefore built
+// without fast-math and with correctly rounded fp32 division.
+#include "common.h"
+#include "kernels.h"
+
+namespace aria {
+
+namespace {
+
+constexpr int TILE_N = 64;  // output channels per workgroup
+constexpr int TILE_K = 64;  // k rows per LDS tile
+constexpr int LDS_STRIDE = TILE_N + 2;  // halfs; the +2 spreads column reads over banks
+
+__device__ __forceinline__ int8_t quant_one(float v, float s, float qmax) {
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, -qmax), qmax);
+    return (int8_t)(int)r;
+}
+
+// Load a TILE_K x TILE_N tile of W (rows k0.., columns n0..) into LDS, zero outside.
+__device__ __forceinline__ void load_tile(half_t (*tile)[LDS_STRIDE], const half_t* __restrict__ w,
+                                          int64_t K, int64_t N, int64_t k0, int64_t n0) {
+    for (int i = threadIdx.x; i < TILE_K * TILE_N; i += blockDim.x) {
+        int r = i / TILE_N, c = i % TILE_N;
+        int64_t k = k0 + r, n = n0 + c;
+        tile[r][c] = (k < K && n < N) ? w[k * N + n] : (half_t)0.0f;
+    }
+}
+
+}  // namespace
+
+// q8: one workgroup per 64 output channels.  Pass 1 reduces max|w| per channel
+// (coalesced along N), pass 2 quantizes 64x64 tiles through LDS and writes each
+// channel's row of Wq contiguously along K (16 bytes per thread).
+__global__ __launch_bounds__(256) void qpack8_kernel(const half_t* __restrict__ w, int64_t K, int64_t N,
+                                                     int8_t* __restrict__ q, half_t* __restrict__ s) {
+    __shared__ float red[4][TILE_N];
+    __shared__ float scale[TILE_N];
+    __shared__ half_t tile[TILE_K][LDS_STRIDE];
+    const int64_t n0 = (int64_t)blockIdx.x * TILE_N;
+    const int c = threadIdx.x % TILE_N, r = threadIdx.x / TILE_N;
+
+    float a = 0.0f;
+    if (n0 + c < N)
+        for (int64_t k = r; k < K; k += 4) a = fmaxf(a, fabsf((float)w[k * N + n0 + c]));
+    red[r][c] = a;
+    __syncthreads();
+    if (r == 0) {
+        a = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+        half_t sh = (half_t)(a / 127.0f);
+        scale[c] = (float)sh;
+        if (n0 + c < N) s[n0 + c] = sh;
+    }
+    __syncthreads();
+
+    // thread -> (channel cn, 16-k segment seg) of the tile
+    const int cn = threadIdx.x / 4, seg = threadIdx.x % 4;
+    for (int64_t k0 = 0; k0 < K; k0 += TILE_K) {
+        load_tile(tile, w, K, N, k0, n0);
+        __syncthreads();
+        const int64_t kb = k0 + seg * 16;
+        if (n0 + cn < N && kb < K) {  // K % 32 == 0, so a 16-k segment is all in or all out
+            const float sc = scale[cn];
+            union { int8_t b[16]; v4i v; } out;
+#pragma unroll
+            for (int i = 0; i < 16; i++) out.b[i] = quant_one((float)tile[seg * 16 + i][cn], sc, 127.0f);
+            *reinterpret_cast<v4i*>(q + (n0 + cn) * K + kb) = out.v;
+        }
+        __syncthreads();
+    }
+}
+
+// q4: one workgroup per 64 output channels; each 64x64 tile holds two k-groups
+// of 32; threads 0..127 own one (channel, group) each: absmax over 32 values,
+// scale, quantize, and one 16-byte store of 32 nibbles.
+__global__ __launch_bounds__(256) void qpack4_kernel(const half_t* __restrict__ w, int64_t K, int64_t N,
+                                                     uint8_t* __restrict__ q4, half_t* __restrict__ s) {
+    __shared__ half_t tile[TILE_K][LDS_STRIDE];
+    const int64_t n0 = (int64_t)blockIdx.x * TILE_N;
+    const int64_t G = K / 32;
+    const int cn = threadIdx.x % TILE_N, g = threadIdx.x / TILE_N;  // g in 0..3, only 0..1 work
+    for (int64_t k0 = 0; k0 < K; k0 += TILE_K) {
+        load_tile(tile, w, K, N, k0, n0);
+        __syncthreads();
+        const int64_t kb = k0 + g * 32;
+        if (g < 2 && n0 + cn < N && kb < K) {
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; i++) a = fmaxf(a, fabsf((float)tile[g * 32 + i][cn]));
+            half_t sh = (half_t)(a / 7.0f);
+            const float sc = (float)sh;
+            union { uint8_t b[16]; v4i v; } out;
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                int lo = quant_one((float)tile[g * 32 + 2 * j][cn], sc, 7.0f);
+                int hi = quant_one((float)tile[g * 32 + 2 * j + 1][cn], sc, 7.0f);
+                out.b[j] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+            }
+            *reinterpret_cast<v4i*>(q4 + (n0 + cn) * (K / 2) + kb / 2) = out.v;
+            s[(n0 + cn) * G + kb / 32] = sh;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_qpack8(const half_t* w, int64_t K, int64_t N, int8_t* q, half_t* s, hipStream_t st) {
+    dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N));
+    hipLaunchKernelGGL(qpack8_kernel, grid, dim3(256), 0, st, w, K, N, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_qpack4(const half_t* w, int64_t K, int64_t N, uint8_t* q4, half_t* s, hipStream_t st) {
+    dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N));
+    hipLaunchKernelGGL(qpack4_kernel, grid, dim3(256), 0, st, w, K, N, q4, s);
+    return hipGetLastError();
+}
+
+}  // namespace aria

@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports every function include/aria_qlinear.h
+declares, and rejects bad arguments on the host before any launch (no GPU
+needed: every call here fails validation, so nothing reaches the device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aria_qlinear.h")
+LIB = os.path.join(ROOT, "quantized_diffusion_transformer_qlinear_amd", "libaria_qlinear.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="HIP library not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aria_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantized_diffusion_transformer_qlinear_amd as m
+    return m
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 9, names
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (aria_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(q):
+    for code in range(-7, 1):
+        assert q.status_string(code) and q.status_string(code) != "unknown status"
+    assert q.status_string(-99) == "unknown status"
+    assert q.lib.aria_abi_version() == 1
+
+
+def test_qpack_bytes(q):
+    assert q.qpack_bytes(8, 0, 1536, 6144) == (1536 * 6144, 2 * 6144)
+    assert q.qpack_bytes(4, 32, 1536, 6144) == (1536 * 6144 // 2, 2 * 6144 * 48)
+    for bits, group in ((8, 32), (4, 0), (4, 64), (2, 32)):
+        with pytest.raises(q.AriaError) as e:
+            q.qpack_bytes(bits, group, 64, 64)
+        assert e.value.code == -4
+    with pytest.raises(q.AriaError) as e:
+        q.qpack_bytes(8, 0, 48, 64)       # K % 32 != 0
+    assert e.value.code == -2
+
+
+def _w8a8(q, x=16, M=64, K=256, N=256, wq=32, sw=48, epi=None, y=4096, ws=1 << 20, ws_bytes=1 << 30):
+    e = ctypes.byref(epi) if epi is not None else None
+    return q.lib.aria_qlinear_w8a8(x, M, K, N, wq, sw, e, y, ws, ws_bytes, None)
+
+
+def test_validation_codes(q):
+    L = q.lib
+    X, W, S, Y, WS = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20  # never dereferenced
+    big = 1 << 40
+    # null pointers
+    assert _w8a8(q, x=None) == -1
+    assert _w8a8(q, wq=None) == -1
+    assert _w8a8(q, y=None) == -1
+    # shapes
+    for M, K, N in ((0, 256, 256), (64, 0, 256), (64, 256, 0), (64, 48, 256), (64, 32768, 256)):
+        assert _w8a8(q, X, M, K, N, W, S, None, Y, WS, big) == -2, (M, K, N)
+    # alignment
+    assert _w8a8(q, X + 2, 64, 256, 256, W, S, None, Y, WS, big) == -3
+    assert _w8a8(q, X, 64, 256, 256, W, S + 8, None, Y, WS, big) == -3
+    # workspace
+    need = q.workspace_bytes(q.ARIA_W8A8, 64, 256, 256)
+    assert need >= 64 * 256 + 128
+    assert _w8a8(q, X, 64, 256, 256, W, S, None, Y, WS, need - 1) == -5
+    assert _w8a8(q, X, 64, 256, 256, W, S, None, Y, None, big) == -5
+    # x overlapping y
+    assert _w8a8(q, X, 64, 256, 256, W, S, None, X + 1024, WS, big) == -7
+    # epilogue options
+    E = q.binding.Epilogue
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 2, 0, None, None, None, None), Y, WS, big) == -4
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 1, None, None, None, None), Y, WS, big) == -4
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, None, 7 << 20, None, None), Y, WS, big) == -1
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(S + 2, 0, 0, None, None, None, None), Y, WS, big) == -3
+    # residual partly overlapping y is rejected, exact aliasing is allowed past validation
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, Y + 512, None, None, None), Y, WS, big) == -7
+    # acc_out only for W8A8; group must be 32 for W4A16
+    ep = E(None, 0, 0, None, None, None, 6 << 20)
+    assert L.aria_qlinear_w8a16(X, 64, 256, 256, W, S, ctypes.byref(ep), Y, None, 0, None) == -4
+    assert L.aria_qlinear_w4a16(X, 64, 256, 256, W, S, 64, None, Y, None, 0, None) == -4
+    assert L.aria_qlinear_w4a16(None, 64, 256, 256, W, S, 32, None, Y, None, 0, None) == -1
+    # packing and activation quantization
+    assert L.aria_qpack(8, 0, None, 64, 64, W, S, None) == -1
+    assert L.aria_qpack(8, 0, X, 64, 64, W + 1, S, None) == -3
+    assert L.aria_qpack(3, 0, X, 64, 64, W, S, None) == -4
+    assert L.aria_qpack(8, 0, X, 64, 64, X + 64, S, None) == -7
+    assert L.aria_quant_act(X, 64, 33, W, S, None) == -2
+    assert L.aria_quant_act(X, 64, 64, None, S, None) == -1
+    assert L.aria_qlinear_workspace_bytes(9, 64, 64, 64) == 0
+    assert L.aria_qlinear_workspace_bytes(0, 64, 40, 64) == 0
