@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized DiT linear layer on one MI355X.
+
+One step = one pass of the three qlinear modes at M = 2048 tokens, DiT width
+1536, on seeded synthetic inputs already resident in HBM:
+  1. W8A8 block chain: QKV 1536->4608, identity-attention stand-in (V slice),
+     out-projection 1536->1536 + residual, MLP-up 1536->6144 + GELU,
+     MLP-down 6144->1536 + residual + alpha*d (alpha = 0.3, unit-norm d);
+     per-token int8 activation quantization before every GEMM;
+  2. W8A16 MLP-up 1536->6144 + bias + GELU;
+  3. W4A16 (signed 4-bit, group 32) 1536->6144.
+Weights are packed once before timing (the fp16 copies are then freed).
+The printed value is the aggregate contraction throughput of the step in TOPS
+(2*M*K*N per linear; int8 and fp16 operations counted alike).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "qlinear TOPS + % of MFMA/HBM roofline (W8A8, W8A16, W4A16) at M=2048"
+PEAK = {"int8": 5000.0, "fp16": 2500.0, "hbm": 8000.0}  # TOPS, TFLOP/s, GB/s (MI355X datasheet, dense)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["common.h", "gemm_w8a8.hip", "gemm_wxa16.hip", "actquant.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_diffusion_transformer_qlinear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def linears(M=2048, W=1536, F=6144):
+    """(name, mode, K, N, extra bytes per call beyond W, scales, X and Y)."""
+    return [
+        ("w8a8.qkv", "w8a8", W, 3 * W, 0),
+        ("w8a8.out", "w8a8", W, W, M * W * 2),              # + residual read
+        ("w8a8.up", "w8a8", W, F, 0),
+        ("w8a8.down", "w8a8", F, W, M * W * 2 + W * 4),     # + residual + d
+        ("w8a16.up", "w8a16", W, F, F * 2),                 # + bias
+        ("w4a16", "w4a16", W, F, 0),
+    ]
+
+
+def algo_bytes(mode, M, K, N, extra):
+    wb = K * N if mode != "w4a16" else K * N // 2
+    sb = N * 2 if mode != "w4a16" else N * (K // 32) * 2
+    return wb + sb + M * K * 2 + M * N * 2 + extra
+
+
+def roofline(mode, M, K, N, extra, us):
+    ops = 2.0 * M * K * N
+    byt = algo_bytes(mode, M, K, N, extra)
+    peak_ops = PEAK["int8"] if mode == "w8a8" else PEAK["fp16"]
+    ai = ops / byt
+    ridge = peak_ops * 1e12 / (PEAK["hbm"] * 1e9)
+    if ai >= ridge:
+        ach = ops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak_ops, "unit": "TFLOP/s", "frac": ach / peak_ops}
+    ach = byt / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"]}
+
+
+def cpu_baseline(inputs, budget_s=12.0):
+    """The oracle, as it stands, on a bounded row sample of the same step."""
+    import numpy as np
+
+    import oracle
+    blk, lin2, x3, w3 = inputs
+    packed = {k: oracle.qpack8(blk[k]) for k in ("qkv", "o", "up", "down")}
+    p2 = oracle.qpack8(lin2.w)
+    p3 = oracle.qpack4(w3, 32)
+    total_ops = sum(2.0 * 2048 * K * N for _, _, K, N, _ in linears())
+    rows_done, chunk, t0 = 0, 16, time.perf_counter()
+    while rows_done < 2048 and time.perf_counter() - t0 < budget_s:
+        r = slice(rows_done, rows_done + chunk)
+        oracle.dit_block_w8a8(blk["h"][r], packed, d=blk["d"], alpha=blk["alpha"])
+        oracle.qlinear_w8a16(lin2.x[r], *p2, bias=lin2.bias, gelu=True)
+        oracle.qlinear_w4a16(x3[r], *p3)
+        rows_done += chunk
+    dt = time.perf_counter() - t0
+    ops = total_ops * rows_done / 2048
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cpu = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    del np
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows_done} of 2048 token rows of every linear of the step "
+                      f"({ops / 1e9:.1f} G ops in {dt:.1f} s; plain C fp64/int64 oracle, OpenMP, {cpu})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the qlinear path is data-parallel over tokens and "
+              "runs unsharded on a single MI355X; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_diffusion_transformer_qlinear_amd as q
+    import synthetic_inputs as si
+    from quantized_diffusion_transformer_qlinear_amd.chain import DitBlockW8A8
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M = si.TOKENS
+
+    def up(a):
+        return torch.from_numpy(a).to(dev)
+
+    # ---- inputs, packed once (fp16 weights released after packing) ----
+    blk = si.dit_block()
+    lin2 = si.mlp_up_w8a16()
+    x3 = si.w4a16_sweep_x()
+    w3 = si.w4a16_w()
+    packed = {}
+    for k in ("qkv", "o", "up", "down"):
+        wd = up(blk[k])
+        packed[k] = q.qpack(8, wd)
+        del wd
+    wd = up(lin2.w)
+    wq2, sw2 = q.qpack(8, wd)
+    del wd
+    wd = up(w3)
+    wq3, sg3 = q.qpack(4, wd)
+    del wd
+    torch.cuda.synchronize()
+    h = up(blk["h"])
+    d = up(blk["d"])
+    alpha = torch.tensor([blk["alpha"]], dtype=torch.float32, device=dev)
+    chain = DitBlockW8A8(packed, M, si.WIDTH, si.MLP, steer_dir=d, steer_alpha=alpha)
+    x2, b2 = up(lin2.x), up(lin2.bias)
+    y2 = torch.empty((M, si.MLP), dtype=torch.float16, device=dev)
+    x3d = up(x3)
+    y3 = torch.empty((M, si.MLP), dtype=torch.float16, device=dev)
+
+    names = ["w8a8.qkv", "attention(copy)", "w8a8.out", "w8a8.up", "w8a8.down", "w8a16.up", "w4a16"]
+
+    def step(evs=None):
+        i = 0
+        if evs is not None:
+            evs[0].record()
+        for _ in chain.stages(h):
+            i += 1
+            if evs is not None:
+                evs[i].record()
+        q.qlinear_w8a16(x2, wq2, sw2, y=y2, bias=b2, gelu=True)
+        if evs is not None:
+            evs[6].record()
+        q.qlinear_w4a16(x3d, wq3, sg3, y=y3)
+        if evs is not None:
+            evs[7].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    per = {n: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps * 1e3
+           for i, n in enumerate(names)}  # us per call
+
+    lin = {n: (mode, K, N, extra) for n, mode, K, N, extra in linears()}
+    total_ops = sum(2.0 * M * K * N for _, K, N, _ in lin.values())
+    value = total_ops / (ms_per_step * 1e-3) / 1e12
+    calls = {}
+    for n, (mode, K, N, extra) in lin.items():
+        rf = roofline(mode, M, K, N, extra, per[n])
+        calls[n] = {"us": round(per[n], 2), "tops": round(2.0 * M * K * N / per[n] / 1e6, 1),
+                    "bound": rf["bound"], "frac": round(rf["frac"], 4),
+                    "launches": 2 if mode == "w8a8" else 1}
+    calls["attention(copy)"] = {"us": round(per["attention(copy)"], 2)}
+    modes = {}
+    for mode, members in (("w8a8_chain", [n for n in lin if n.startswith("w8a8")]), ("w8a16", ["w8a16.up"]),
+                          ("w4a16", ["w4a16"])):
+        us = sum(per[n] for n in members) + (per["attention(copy)"] if mode == "w8a8_chain" else 0.0)
+        ops = sum(2.0 * M * lin[n][1] * lin[n][2] for n in members)
+        modes[mode] = {"us": round(us, 2), "tops": round(ops / us / 1e6, 1)}
+
+    # dominant kernel: the largest single-launch call of the step
+    dom = max((n for n in lin if lin[n][0] != "w8a8"), key=lambda n: per[n])
+    mode, K, N, extra = lin[dom]
+    rf = roofline(mode, M, K, N, extra, per[dom])
+    rf["kernel"] = f"{dom} ({'gemm_wxa16_tiled_kernel<8,128,128>' if mode == 'w8a16' else 'gemm_wxa16_tiled_kernel<4,128,128>'})"
+    rf["traffic"] = None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+        if t.get("kernel_hash") == kernel_hash() and dom in t.get("per_launch_bytes", {}):
+            rf["traffic"] = t["per_launch_bytes"][dom]
+    except (OSError, ValueError):
+        pass
+    for k in ("achieved", "frac"):
+        rf[k] = round(rf[k], 4 if k == "frac" else 1)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8+f16",
+        "data": "synthetic: seeded N(0,1) fp16 activations, N(0,0.02) fp16 weights (stand-ins for SA3 DiT tensors)",
+        "config": {"workload": "dit_qlinear_m2048: W8A8 DiT block chain (width 1536: QKV 4608, out 1536 + residual, "
+                               "MLP-up 6144 + GELU, MLP-down 1536 + residual + 0.3*d) + W8A16 MLP-up 1536x6144 "
+                               "(+bias, GELU) + W4A16 g32 1536x6144",
+                   "tokens": M, "width": si.WIDTH, "mlp": si.MLP, "ops_per_step": total_ops},
+        "roofline": rf,
+        "modes": modes,
+        "calls": calls,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

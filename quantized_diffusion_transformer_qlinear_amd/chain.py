@@ -1,0 +1,73 @@
+"""The W8A8 diffusion-transformer block chain built from qlinear calls.
+
+The aria pages run the denoising step's transformer blocks at W8A8 and add the
+steering direction to one block's residual stream (project page, "Results":
+"Steering is real, inside a narrow window"; the CLI form
+``--steer residual:<block>:<file>:<alpha>:<steps>``).  The block here is
+QKV -> attention -> out-projection (+ residual) -> MLP-up (GELU) -> MLP-down
+(+ residual + alpha * d).  The attention core is not a quantized linear; it is
+stood in for by identity attention (each token attends only to itself, so the
+attention output is the V third of the QKV output), which keeps the chain
+data-dependent and row-local.  The stand-in is a strided device-to-device copy
+(hipMemcpy2DAsync); every arithmetic step runs in the qlinear kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import binding as B
+
+_hip = ctypes.CDLL("libamdhip64.so")
+_hip.hipMemcpy2DAsync.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+_hip.hipMemcpy2DAsync.restype = ctypes.c_int
+_D2D = 3  # hipMemcpyDeviceToDevice
+
+
+def copy_columns(dst, src, col0: int, ncols: int, stream=None):
+    """dst[:, :] = src[:, col0:col0+ncols] for fp16 row-major tensors (device copy)."""
+    M = src.shape[0]
+    es = src.element_size()
+    rc = _hip.hipMemcpy2DAsync(dst.data_ptr(), dst.shape[1] * es, src.data_ptr() + col0 * es, src.shape[1] * es,
+                               ncols * es, M, _D2D, B._stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy2DAsync failed ({rc})")
+
+
+class DitBlockW8A8:
+    """Preallocated W8A8 block: ``run(h)`` enqueues the chain on the stream and
+    returns the block output (fp16 [M][width])."""
+
+    def __init__(self, packed: dict, M: int, width: int, mlp: int, steer_dir=None, steer_alpha=None):
+        import torch
+        dev = packed["qkv"][0].device
+        self.packed, self.M, self.width, self.mlp = packed, M, width, mlp
+        self.steer_dir, self.steer_alpha = steer_dir, steer_alpha
+        f16 = torch.float16
+        self.qkv = torch.empty((M, 3 * width), dtype=f16, device=dev)
+        self.a = torch.empty((M, width), dtype=f16, device=dev)
+        self.h1 = torch.empty((M, width), dtype=f16, device=dev)
+        self.u = torch.empty((M, mlp), dtype=f16, device=dev)
+        self.out = torch.empty((M, width), dtype=f16, device=dev)
+        need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, 1) for k in (width, mlp))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def stages(self, h, stream=None):
+        """Yields after each stage (for per-stage timing or checks)."""
+        p = self.packed
+        B.qlinear_w8a8(h, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)
+        yield "qkv"
+        copy_columns(self.a, self.qkv, 2 * self.width, self.width, stream)
+        yield "attention"
+        B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)
+        yield "out"
+        B.qlinear_w8a8(self.h1, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)
+        yield "up"
+        B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
+                       steer_dir=self.steer_dir, steer_alpha=self.steer_alpha, stream=stream)
+        yield "down"
+
+    def run(self, h, stream=None):
+        for _ in self.stages(h, stream):
+            pass
+        return self.out

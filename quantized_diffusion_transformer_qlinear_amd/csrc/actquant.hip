@@ -5,8 +5,11 @@
 // activations are quantized per token (row) on the fly:
 //   s_a[m] = fp16_RNE(max_k |x[m][k]| / 127),  xq[m][k] = clamp(RNE(x / s_a), -127, 127)
 // with the same fp32 route as the weight packer (bit-exact with the fp64
-// definition; see qpack.hip).  One wave per token row: 16-byte loads along K,
-// an in-register absmax, a cross-lane max, then 8-byte int8 stores.
+// definition; see qpack.hip).  One wave per token row: every 16-byte load of
+// the row is issued before any is used (bounds-checked buffer loads, so the
+// K tail reads zeros without a branch), an in-register absmax, a cross-lane
+// max, then 8-byte int8 stores (out-of-range stores are dropped by the buffer
+// range check).
 #include "common.h"
 #include "kernels.h"
 
@@ -23,40 +26,40 @@ __device__ __forceinline__ float wave_max(float v) {
 }  // namespace
 
 template <int CH>  // CH 16-byte chunks per lane kept in registers (K <= CH * 512)
-__global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict__ x, int64_t M, int64_t K,
+__global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict__ x, int M, int K,
                                                        int8_t* __restrict__ xq, half_t* __restrict__ sa) {
     const int lane = threadIdx.x % WAVE;
-    const int64_t m = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+    const int m = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
     if (m >= M) return;
-    const half_t* row = x + m * K;
+    const rsrc_t rx = make_rsrc(x + (int64_t)m * K, (uint32_t)K * 2);
+    const rsrc_t rq = make_rsrc(xq + (int64_t)m * K, (uint32_t)K);
     v8h v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; c++) v[c] = __builtin_bit_cast(v8h, buf_load16(rx, (uint32_t)(c * 512 + lane * 8) * 2));
     float a = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CH; c++) {
-        const int64_t k = (int64_t)c * 512 + lane * 8;  // K % 32 == 0: a chunk is all in or all out
-        if (k < K) {
-            v[c] = *reinterpret_cast<const v8h*>(row + k);
+    for (int c = 0; c < CH; c++)
 #pragma unroll
-            for (int e = 0; e < 8; e++) a = fmaxf(a, fabsf((float)v[c][e]));
-        }
-    }
+        for (int e = 0; e < 8; e++) a = fmaxf(a, fabsf((float)v[c][e]));
     a = wave_max(a);
     const half_t sh = (half_t)(a / 127.0f);
     const float s = (float)sh;
     if (lane == 0) sa[m] = sh;
 #pragma unroll
     for (int c = 0; c < CH; c++) {
-        const int64_t k = (int64_t)c * 512 + lane * 8;
-        if (k < K) {
-            union { int8_t b[8]; uint2 u; } out;
+        u32 w[2];
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                float r = (s == 0.0f) ? 0.0f : __builtin_rintf((float)v[c][e] / s);
+        for (int h = 0; h < 2; h++) {
+            u32 packed = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float r = (s == 0.0f) ? 0.0f : __builtin_rintf((float)v[c][4 * h + e] / s);
                 r = fminf(fmaxf(r, -127.0f), 127.0f);
-                out.b[e] = (int8_t)(int)r;
+                packed |= ((u32)(int)r & 0xFFu) << (8 * e);
             }
-            *reinterpret_cast<uint2*>(xq + m * K + k) = out.u;
+            w[h] = packed;
         }
+        buf_store8(v2u{w[0], w[1]}, rq, (uint32_t)(c * 512 + lane * 8));
     }
 }
 
@@ -64,12 +67,16 @@ hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, ha
     const int rows_per_block = 4;
     dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(rows_per_block * WAVE);
     const int64_t ch = (K + 511) / 512;
-    if (ch <= 1) hipLaunchKernelGGL(actquant_kernel<1>, grid, block, 0, st, x, M, K, xq, sa);
-    else if (ch <= 2) hipLaunchKernelGGL(actquant_kernel<2>, grid, block, 0, st, x, M, K, xq, sa);
-    else if (ch <= 4) hipLaunchKernelGGL(actquant_kernel<4>, grid, block, 0, st, x, M, K, xq, sa);
-    else if (ch <= 8) hipLaunchKernelGGL(actquant_kernel<8>, grid, block, 0, st, x, M, K, xq, sa);
-    else if (ch <= 16) hipLaunchKernelGGL(actquant_kernel<16>, grid, block, 0, st, x, M, K, xq, sa);
-    else if (ch <= 32) hipLaunchKernelGGL(actquant_kernel<32>, grid, block, 0, st, x, M, K, xq, sa);
+    const int m = (int)M, k = (int)K;
+    if (ch <= 1) hipLaunchKernelGGL(actquant_kernel<1>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 2) hipLaunchKernelGGL(actquant_kernel<2>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 3) hipLaunchKernelGGL(actquant_kernel<3>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 4) hipLaunchKernelGGL(actquant_kernel<4>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 6) hipLaunchKernelGGL(actquant_kernel<6>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 8) hipLaunchKernelGGL(actquant_kernel<8>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 12) hipLaunchKernelGGL(actquant_kernel<12>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 16) hipLaunchKernelGGL(actquant_kernel<16>, grid, block, 0, st, x, m, k, xq, sa);
+    else if (ch <= 32) hipLaunchKernelGGL(actquant_kernel<32>, grid, block, 0, st, x, m, k, xq, sa);
     else return hipErrorInvalidValue;  // K > 16384: rejected on the host before this point
     return hipGetLastError();
 }

@@ -21,7 +21,8 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int check_shape(int64_t M, int64_t K, int64_t N) {
     if (M < 1 || N < 1 || K < 32 || (K % 32) != 0) return ARIA_E_SHAPE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxK) return ARIA_E_SHAPE;
-    if (M * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40)) return ARIA_E_SHAPE;
+    // packed weights of one linear are addressed with 32-bit offsets
+    if (M * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40) || N * K >= ((int64_t)1 << 31)) return ARIA_E_SHAPE;
     return ARIA_OK;
 }
 
@@ -143,8 +144,8 @@ int aria_qlinear_w8a8(const void* x, int64_t M, int64_t K, int64_t N, const int8
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if ((rc = hip_status(launch_actquant(static_cast<const half_t*>(x), M, K, xq, sa, st))) != ARIA_OK) return rc;
-    return hip_status(launch_gemm_w8a8(xq, wq, sa, static_cast<const half_t*>(sw), static_cast<half_t*>(y),
-                                       (int)M, (int)N, (int)K, e, st));
+    return hip_status(launch_gemm_tiled(0, xq, wq, static_cast<const half_t*>(sw), sa, static_cast<half_t*>(y),
+                                        (int)M, (int)N, (int)K, e, st));
 }
 
 static int wxa16(int bits, const void* x, int64_t M, int64_t K, int64_t N, const void* wq, const void* s,

@@ -14,6 +14,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef uint32_t u32;
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
@@ -50,6 +52,22 @@ __device__ __forceinline__ float epilogue_apply(float y, int64_t idx, int n, con
     if (e.residual) y += (float)e.residual[idx];
     if (alpha != 0.0f) y += alpha * e.steer_dir[n];
     return y;
+}
+
+// Buffer resources: 32-bit offsets with hardware range checking; a load past
+// num_records returns zero and a store past it is dropped, which keeps ragged
+// edges branch-free.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(v2u v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
 
 // XCD-aware remap of a linear workgroup id: the hardware deals workgroups

@@ -1,0 +1,459 @@
+// a3+a4+a5 — the tiled quantized GEMM for M > 64, all three modes, with the
+// fused epilogue.
+//
+// What is computed (aria project page, "What aria is" / "Results": weights
+// stored at 8 or 4 bits; W8A8 runs 8-bit arithmetic on integer matrix units):
+//   W8A8 : acc = sum_k Xq[m][k] * Wq[n][k] (exact int32);  y = acc * s_a[m] * s_w[n]
+//   W8A16: acc = sum_k X[m][k] * Wq[n][k]  (fp32; int8 -> fp16 is exact);  y = acc * s_w[n]
+//   W4A16: acc = sum_k X[m][k] * fp16(q4[n][k] * s_g[n][k/32])  (fp32);  y = acc
+// then y -> + bias -> GELU -> + residual -> + alpha d -> fp16.
+//
+// Design (gfx950): a workgroup of WM x WN waves owns a BM x BN output tile;
+// each wave owns (BM/WM) x (BN/WN) as 32x32 blocks on the matrix cores
+// (v_mfma_i32_32x32x32_i8 or v_mfma_f32_32x32x16_f16).  Both operands live in
+// LDS as rows of 128 bytes (128 int8 k or 64 fp16 k) plus a 16-byte pad that
+// spreads the 32 rows of an operand fragment over all banks; a K-step is 4
+// MFMA sub-steps in every mode.  The next tile is fetched two K-steps ahead
+// into registers with bounds-checked buffer loads (rows past M/N and k past K
+// read as zero), and its decode + LDS store is split over the 4 sub-steps of
+// the current K-step so that it overlaps the matrix work; one barrier per
+// K-step.  Packed weights are decoded in registers: int8 -> fp16 and nibble
+// -> fp16 by building the fp16 pattern 0x6400 | u (= 1024 + u) and
+// subtracting the bias, two values per packed-half instruction.
+#include "common.h"
+#include "kernels.h"
+
+namespace aria {
+
+namespace {
+
+// 16 int8 (4 dwords) -> 16 fp16, exact: (b ^ 0x80) = q + 128 -> fp16(0x6400 | u) - 1152.
+__device__ __forceinline__ void dec8(v4i w, v4i& lo, v4i& hi) {
+    const v2h bias = {(half_t)1152.0f, (half_t)1152.0f};
+    u32 o[8];
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        const u32 u = (u32)w[d] ^ 0x80808080u;
+        const u32 p0 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // bytes: u0, 64, u1, 64
+        const u32 p1 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // bytes: u2, 64, u3, 64
+        v2h h0 = __builtin_bit_cast(v2h, p0) - bias;
+        v2h h1 = __builtin_bit_cast(v2h, p1) - bias;
+        o[2 * d] = __builtin_bit_cast(u32, h0);
+        o[2 * d + 1] = __builtin_bit_cast(u32, h1);
+    }
+    lo = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    hi = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+}
+
+// 32 nibbles (4 dwords; even k in the low nibble) -> 32 fp16 values fp16(q * s):
+// (n ^ 8) = q + 8 -> fp16(0x6400 | u) - 1032 = q (exact) -> times s (one rounding).
+__device__ __forceinline__ void dec4(v4i w, half_t s, v4i out[4]) {
+    const v2h bias = {(half_t)1032.0f, (half_t)1032.0f};
+    const v2h sc = {s, s};
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        const u32 u = (u32)w[d] ^ 0x88888888u;
+        const u32 t0 = u & 0x0F0F0F0Fu;          // bytes: k0 k2 k4 k6
+        const u32 t1 = (u >> 4) & 0x0F0F0F0Fu;   // bytes: k1 k3 k5 k7
+        u32 o[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            // k = 2j (byte j of t0) in the low half, k = 2j+1 (byte j of t1) in the high half
+            const u32 sel = 0x0C000C00u | (u32)j | ((u32)(4 + j) << 16);
+            const u32 p = __builtin_amdgcn_perm(t1, t0, sel) | 0x64006400u;
+            v2h h = (__builtin_bit_cast(v2h, p) - bias) * sc;
+            o[j] = __builtin_bit_cast(u32, h);
+        }
+        out[d] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    }
+}
+
+template <int MODE>
+struct ModeT;
+template <>
+struct ModeT<0> {  // W8A8
+    static constexpr int KSTEP = 128;        // k per 128-byte row
+    static constexpr int AEB = 1;            // A element bytes
+    static constexpr int KPB = 16;           // k per 16-byte packed weight chunk
+    static constexpr int BCH = 8;            // packed weight chunks per row per K-step
+    typedef v16i acc_t;
+};
+template <>
+struct ModeT<1> {  // W8A16
+    static constexpr int KSTEP = 64, AEB = 2, KPB = 16, BCH = 4;
+    typedef v16f acc_t;
+};
+template <>
+struct ModeT<2> {  // W4A16
+    static constexpr int KSTEP = 64, AEB = 2, KPB = 32, BCH = 2;
+    typedef v16f acc_t;
+};
+
+}  // namespace
+
+template <int MODE, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* __restrict__ Aptr, const uint8_t* __restrict__ Bq,
+                                                         const half_t* __restrict__ S, const half_t* __restrict__ sa,
+                                                         half_t* Y, int M, int N, int K, Epi epi) {
+    using T = ModeT<MODE>;
+    constexpr int NT = WM * WN * WAVE;
+    constexpr int ROWB = 144;                    // LDS bytes per row (128 + pad)
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int NA = BM * 8;                   // 16-byte A chunks per K-step
+    constexpr int NB = BN * T::BCH;              // 16-byte packed B chunks per K-step
+    constexpr int LA = NA / NT;
+    constexpr int LB = (NB + NT - 1) / NT;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && NA % NT == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
+
+    const int ntm = (M + BM - 1) / BM;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int tm = bid % ntm, tn = bid / ntm;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int wm = wave / WN, wn = wave % WN;
+
+    const uint32_t abytes = (uint32_t)M * (uint32_t)K * T::AEB;
+    const uint32_t browb = MODE == 2 ? (uint32_t)K / 2 : (uint32_t)K;
+    const rsrc_t ra = make_rsrc(Aptr, abytes);
+    const rsrc_t rb = make_rsrc(Bq, (uint32_t)N * browb);
+    const int G = K / 32;
+
+    // per-thread chunk coordinates (fixed across K-steps)
+    v4i RA[LA], RB[LB > 0 ? LB : 1];
+    half_t RS[LB > 0 ? LB : 1];
+
+    auto load_a = [&](int kt, int i) {
+        const int c = tid + i * NT, row = c / 8, ch = c % 8;
+        const int k = kt * T::KSTEP + ch * (16 / T::AEB);
+        const uint32_t off = (uint32_t)(m0 + row) * (uint32_t)K * T::AEB + (uint32_t)k * T::AEB;
+        RA[i] = buf_load16(ra, k < K && m0 + row < M ? off : OOB);
+    };
+    // threads past the last B chunk (NB not a multiple of 256) redo chunk c % NB:
+    // the same bytes land at the same LDS address, which keeps the loop branch-free
+    auto load_b = [&](int kt, int i) {
+        const int c = (tid + i * NT) % NB, row = c / T::BCH, ch = c % T::BCH;
+        const int k = kt * T::KSTEP + ch * T::KPB;
+        const bool in = k < K && n0 + row < N;
+        const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : k);
+        RB[i] = buf_load16(rb, in ? off : OOB);
+        if (MODE == 2) RS[i] = S[(int64_t)min(n0 + row, N - 1) * G + min(k, K - 32) / 32];
+    };
+    auto store_a = [&](int buf, int i) {
+        const int c = tid + i * NT, row = c / 8, ch = c % 8;
+        *reinterpret_cast<v4i*>(&lds[buf][row * ROWB + ch * 16]) = RA[i];
+    };
+    auto store_b = [&](int buf, int i) {
+        const int c = (tid + i * NT) % NB;
+        const int row = c / T::BCH, ch = c % T::BCH;
+        char* dst = &lds[buf][(BM + row) * ROWB + ch * (T::KPB * 2 / (MODE == 0 ? 2 : 1))];
+        if constexpr (MODE == 0) {
+            *reinterpret_cast<v4i*>(dst) = RB[i];
+        } else if constexpr (MODE == 1) {
+            v4i lo, hi;
+            dec8(RB[i], lo, hi);
+            reinterpret_cast<v4i*>(dst)[0] = lo;
+            reinterpret_cast<v4i*>(dst)[1] = hi;
+        } else {
+            v4i o[4];
+            dec4(RB[i], RS[i], o);
+#pragma unroll
+            for (int q = 0; q < 4; q++) reinterpret_cast<v4i*>(dst)[q] = o[q];
+        }
+    };
+    auto load_part = [&](int kt, int p) {
+#pragma unroll
+        for (int i = p; i < LA; i += 4) load_a(kt, i);
+#pragma unroll
+        for (int i = p; i < LB; i += 4) load_b(kt, i);
+    };
+    auto store_part = [&](int buf, int p) {
+#pragma unroll
+        for (int i = p; i < LA; i += 4) store_a(buf, i);
+#pragma unroll
+        for (int i = p; i < LB; i += 4) store_b(buf, i);
+    };
+
+    typename T::acc_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = typename T::acc_t{};
+
+    const int nk = (K + T::KSTEP - 1) / T::KSTEP;
+#pragma unroll
+    for (int p = 0; p < 4; p++) load_part(0, p);
+#pragma unroll
+    for (int p = 0; p < 4; p++) store_part(0, p);
+#pragma unroll
+    for (int p = 0; p < 4; p++) load_part(1, p);
+    __syncthreads();
+
+    const int arow = (wm * WTM + lane % 32) * ROWB + (lane / 32) * 16;
+    const int brow = (BM + wn * WTN + lane % 32) * ROWB + (lane / 32) * 16;
+    v4i fa[2][FM], fb[2][FN];
+    auto read_frags = [&](const char* L, int p, int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) fa[slot][i] = *reinterpret_cast<const v4i*>(L + arow + i * 32 * ROWB + p * 32);
+#pragma unroll
+        for (int j = 0; j < FN; j++) fb[slot][j] = *reinterpret_cast<const v4i*>(L + brow + j * 32 * ROWB + p * 32);
+    };
+    // The loop body has no branches: the last K-steps load past K (zero-fill,
+    // no memory traffic) and store into the idle buffer, which nothing reads.
+    for (int kt = 0; kt < nk; kt++) {
+        const int cur = kt & 1;
+        const char* L = lds[cur];
+        read_frags(L, 0, 0);
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            if (p < 3) read_frags(L, p + 1, (p + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++) {
+                    if constexpr (MODE == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[p & 1][i], fb[p & 1][j], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fa[p & 1][i]),
+                                                                           __builtin_bit_cast(v8h, fb[p & 1][j]),
+                                                                           acc[i][j], 0, 0, 0);
+                }
+            store_part(cur ^ 1, p);
+            load_part(kt + 2, p);
+        }
+#if defined(ARIA_SCHED) && ARIA_SCHED == 1
+        __builtin_amdgcn_iglp_opt(0);
+#elif defined(ARIA_SCHED) && ARIA_SCHED == 2
+        __builtin_amdgcn_iglp_opt(1);
+#elif defined(ARIA_SCHED) && ARIA_SCHED == 3
+        {
+            constexpr int NMF = FM * FN;
+            constexpr int NW = LA + LB * (MODE == 0 ? 1 : (MODE == 1 ? 2 : 4));   // ds_write per K-step
+            constexpr int NL = LA + LB;                                            // buffer loads per K-step
+            __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+            for (int sp = 0; sp < 4; sp++)
+#pragma unroll
+                for (int m = 0; m < NMF; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (sp < 3 && m < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, MODE == 2 ? 3 : 2, 0);
+                    if ((sp * NMF + m) % ((4 * NMF + NW - 1) / NW) == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    if ((sp * NMF + m) % ((4 * NMF + NL - 1) / NL) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+        }
+#endif
+        __syncthreads();
+    }
+
+    // Epilogue.  Each wave stages one 32-row block-row of its raw accumulators
+    // at a time in its own slice of the (now idle) LDS, transposing the 32x32
+    // MFMA layout (register r of lane l = row 8*(r/4) + 4*(l/32) + r%4, column
+    // l%32) into rows; each lane then owns 8 consecutive columns of one row,
+    // so scales, bias, residual, d and the fp16 output move as 16-byte
+    // vectors.  A row stride of WTN + 8 words puts the two 32-lane halves of a
+    // staging write on disjoint banks.
+    constexpr int SROW = WTN + 8;
+    constexpr int CPRW = WTN / 8;                         // 8-column chunks per staged row
+    constexpr int TASKS = 32 * CPRW / WAVE;               // chunks per lane per block-row
+    static_assert((32 * CPRW) % WAVE == 0, "epilogue chunks must split over the wave");
+    static_assert(WM * WN * 32 * SROW * 4 <= (int)sizeof(lds), "epilogue staging must fit in LDS");
+    uint32_t* stage = reinterpret_cast<uint32_t*>(&lds[0][0]) + wave * 32 * SROW;
+    const float alpha = load_alpha(epi);
+    const bool vec_ok = (N % 8) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int rr = 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                // copy the element out first: a bit cast of a vector-element
+                // lvalue reads the vector's first element, not element r
+                const auto val = acc[i][j][r];
+                stage[rr * SROW + j * 32 + lane % 32] = __builtin_bit_cast(uint32_t, val);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TASKS; t++) {
+            const int task = lane + t * WAVE, rr = task / CPRW, cc = task % CPRW;
+            const int row = m0 + wm * WTM + i * 32 + rr, col = n0 + wn * WTN + cc * 8;
+            if (row >= M || col >= N) continue;
+            // read with the element type the staging stores used (a vector-typed
+            // load of scalar-typed stores would let alias analysis drop them)
+            uint32_t raw[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) raw[e] = stage[rr * SROW + cc * 8 + e];
+            const v4u lo = {raw[0], raw[1], raw[2], raw[3]}, hi = {raw[4], raw[5], raw[6], raw[7]};
+            const int64_t base = (int64_t)row * N + col;
+            if (vec_ok && col + 8 <= N) {
+                float v[8];
+                if constexpr (MODE == 0) {
+                    if (epi.acc_out) {
+                        reinterpret_cast<v4u*>(epi.acc_out + base)[0] = lo;
+                        reinterpret_cast<v4u*>(epi.acc_out + base)[1] = hi;
+                    }
+                    const float sr = (float)sa[row];
+                    const v8h sw8 = *reinterpret_cast<const v8h*>(S + col);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) v[e] = (float)(int32_t)raw[e] * sr * (float)sw8[e];
+                } else if constexpr (MODE == 1) {
+                    const v8h sw8 = *reinterpret_cast<const v8h*>(S + col);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]) * (float)sw8[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]);
+                }
+                if (epi.bias) {
+                    const v8h b8 = *reinterpret_cast<const v8h*>(epi.bias + col);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) v[e] += (float)b8[e];
+                }
+                if (epi.gelu) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) v[e] = gelu_tanh(v[e]);
+                }
+                if (epi.residual) {
+                    const v8h r8 = *reinterpret_cast<const v8h*>(epi.residual + base);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) v[e] += (float)r8[e];
+                }
+                if (alpha != 0.0f) {
+                    const v4f d0 = *reinterpret_cast<const v4f*>(epi.steer_dir + col);
+                    const v4f d1 = *reinterpret_cast<const v4f*>(epi.steer_dir + col + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        v[e] += alpha * d0[e];
+                        v[e + 4] += alpha * d1[e];
+                    }
+                }
+                v8h out;
+#pragma unroll
+                for (int e = 0; e < 8; e++) out[e] = (half_t)v[e];
+                *reinterpret_cast<v8h*>(Y + base) = out;
+            } else {
+                // ragged right edge (or N % 8 != 0): element by element
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    if (col + e >= N) break;
+                    const int64_t idx = base + e;
+                    float v;
+                    if constexpr (MODE == 0) {
+                        if (epi.acc_out) epi.acc_out[idx] = (int32_t)raw[e];
+                        v = (float)(int32_t)raw[e] * (float)sa[row] * (float)S[col + e];
+                    } else if constexpr (MODE == 1) {
+                        v = __builtin_bit_cast(float, raw[e]) * (float)S[col + e];
+                    } else {
+                        v = __builtin_bit_cast(float, raw[e]);
+                    }
+                    Y[idx] = (half_t)epilogue_apply(v, idx, col + e, epi, alpha);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side: tile choice and launch
+// ---------------------------------------------------------------------------
+namespace {
+
+struct TileCfg {
+    int bm, bn, wm, wn;
+};
+
+// Candidate macro tiles.  The choice balances CU fill (whole waves of tiles
+// over the CUs) against per-tile efficiency: a wave tile of a x b 32x32 blocks
+// reads (a + b) fragments from LDS for a * b MFMAs, and 8-wave workgroups put
+// two waves on every SIMD so one can issue while the other waits.
+constexpr TileCfg kTiles[] = {
+    {256, 192, 4, 2}, {256, 192, 2, 2}, {256, 256, 4, 2}, {256, 128, 4, 2}, {128, 256, 2, 4},
+    {128, 192, 2, 2}, {128, 128, 2, 2}, {64, 192, 2, 2}, {128, 64, 2, 2}, {64, 128, 2, 2}, {64, 64, 2, 2}};
+
+int num_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        hipDeviceProp_t p;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess) cus = p.multiProcessorCount;
+        if (cus <= 0) cus = 256;
+    }
+    return cus;
+}
+
+TileCfg pick_tile(int M, int N) {
+    const char* env = getenv("ARIA_QLINEAR_TILE");  // "BMxBNxWMxWN" tuning override
+    if (env) {
+        int bm = 0, bn = 0, wm = 0, wn = 0;
+        if (sscanf(env, "%dx%dx%dx%d", &bm, &bn, &wm, &wn) == 4)
+            for (const TileCfg& t : kTiles)
+                if (t.bm == bm && t.bn == bn && t.wm == wm && t.wn == wn) return t;
+    }
+    const int cus = num_cus();
+    double best = 1e300;
+    TileCfg pick = kTiles[0];
+    for (const TileCfg& t : kTiles) {
+        const double a = t.bm / t.wm / 32.0, b = t.bn / t.wn / 32.0;
+        const double lds_eff = fmin(1.0, 1.5 * (a * b) / (a + b));       // LDS fragment traffic per MFMA
+        const double occ_eff = (t.wm * t.wn >= 8 || t.bm * t.bn <= 128 * 128) ? 1.0 : 0.8;  // latency hiding
+        const long tiles = (long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+        const long waves = (tiles + cus - 1) / cus;
+        const double cost = (double)waves * t.bm * t.bn / (lds_eff * occ_eff);
+        if (cost < best) best = cost, pick = t;
+    }
+    return pick;
+}
+
+template <int MODE, int BM, int BN, int WM, int WN>
+hipError_t launch_one(const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y, int M, int N,
+                      int K, const Epi& e, hipStream_t st) {
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_tiled_kernel<MODE, BM, BN, WM, WN>), dim3(tiles), dim3(WM * WN * WAVE), 0, st, a, b, s,
+                       sa, y, M, N, K, e);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(TileCfg t, const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y,
+                       int M, int N, int K, const Epi& e, hipStream_t st) {
+#define ARIA_TILE(BM_, BN_, WM_, WN_)                          \
+    if (t.bm == BM_ && t.bn == BN_ && t.wm == WM_ && t.wn == WN_) \
+        return launch_one<MODE, BM_, BN_, WM_, WN_>(a, b, s, sa, y, M, N, K, e, st);
+    ARIA_TILE(256, 192, 4, 2) ARIA_TILE(256, 192, 2, 2) ARIA_TILE(256, 256, 4, 2) ARIA_TILE(256, 128, 4, 2)
+    ARIA_TILE(128, 256, 2, 4) ARIA_TILE(128, 192, 2, 2) ARIA_TILE(128, 128, 2, 2) ARIA_TILE(64, 192, 2, 2)
+    ARIA_TILE(128, 64, 2, 2) ARIA_TILE(64, 128, 2, 2) ARIA_TILE(64, 64, 2, 2)
+#undef ARIA_TILE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half_t* s, const half_t* sa, half_t* y,
+                             int M, int N, int K, const Epi& epi, hipStream_t st) {
+    // 32-bit buffer offsets: split very tall problems into row blocks
+    const int64_t aeb = mode == 0 ? 1 : 2;
+    const int64_t max_rows = ((int64_t)1 << 31) / ((int64_t)K * aeb) / 256 * 256;
+    const TileCfg t = pick_tile(M > max_rows ? (int)max_rows : M, N);
+    const uint8_t* b = static_cast<const uint8_t*>(bq);
+    for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
+        const int rows = (int)((M - r0) < max_rows ? (M - r0) : max_rows);
+        Epi e = epi;
+        if (e.residual) e.residual += r0 * N;
+        if (e.acc_out) e.acc_out += r0 * N;
+        const char* ar = static_cast<const char*>(a) + r0 * K * aeb;
+        const half_t* sar = sa ? sa + r0 : nullptr;
+        half_t* yr = y + r0 * N;
+        hipError_t err;
+        if (mode == 0) err = launch_mode<0>(t, ar, b, s, sar, yr, rows, N, K, e, st);
+        else if (mode == 1) err = launch_mode<1>(t, ar, b, s, sar, yr, rows, N, K, e, st);
+        else err = launch_mode<2>(t, ar, b, s, sar, yr, rows, N, K, e, st);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace aria

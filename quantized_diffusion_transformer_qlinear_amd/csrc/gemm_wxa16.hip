@@ -9,11 +9,8 @@
 //   W4A16: y = epilogue(sum_k x[m][k] * fp16(q4[n][k] * s_g[n][k/32]))
 //          (nibble -> signed int -> times its group scale, one fp16 rounding)
 //
-// Two kernels:
-//  - tiled (M > 64): a workgroup of 2x2 waves owns a BM x BN output tile; per
-//    64-k step it loads X (16 B per lane) and the packed weights, decodes the
-//    weights while writing them to double-buffered LDS as fp16, and runs
-//    v_mfma_f32_32x32x16_f16 on 32x32 blocks.
+// M > 64 runs the tiled kernel (gemm_tiled.hip); this file holds the kernel
+// for small M:
 //  - skinny (M <= 64, bandwidth-bound): 4 waves per 16 output channels split K
 //    four ways; each lane streams 16-byte runs of one channel's packed row and
 //    decodes them straight into v_mfma_f32_16x16x32_f16 operands (no LDS for
@@ -52,134 +49,7 @@ __device__ __forceinline__ void decode4(v4i w, float s, v8h out[4]) {
     }
 }
 
-template <int BITS, int BM, int BN, int WM, int WN>
-struct TCfg {
-    static constexpr int BK = 64;               // fp16 k per step
-    static constexpr int NT = WM * WN * WAVE;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int LDK = BK + 8;          // halfs per LDS row (+16 B staggers banks)
-    static constexpr int CPR_A = BK / 8;        // 16-byte chunks per X row
-    static constexpr int KPC = BITS == 8 ? 16 : 32;  // k per 16-byte weight chunk
-    static constexpr int CPR_B = BK / KPC;      // weight chunks per row
-    static constexpr int NA = BM * CPR_A, NB = BN * CPR_B;  // chunks per tile
-    static constexpr int LA = (NA + NT - 1) / NT, LB = (NB + NT - 1) / NT;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "");
-    static_assert(NA % NT == 0, "");
-};
-
 }  // namespace
-
-template <int BITS, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * WAVE) void gemm_wxa16_tiled_kernel(
-    const half_t* __restrict__ X, const uint8_t* __restrict__ Bq, const half_t* __restrict__ S,
-    half_t* Y, int M, int N, int K, Epi epi) {
-    using C = TCfg<BITS, BM, BN, WM, WN>;
-    __shared__ __attribute__((aligned(16))) half_t As[2][BM * C::LDK];
-    __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * C::LDK];
-
-    const int ntm = (M + BM - 1) / BM;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int tm = bid % ntm, tn = bid / ntm;
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-    const int wm = wave / WN, wn = wave % WN;
-    const int64_t rowbytes = BITS == 8 ? (int64_t)K : (int64_t)K / 2;
-    const int G = K / 32;
-
-    v16f acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) acc[i][j] = v16f{};
-
-    v4i ra[C::LA], rb[C::LB];
-    float rs[C::LB];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < C::LA; i++) {
-            const int c = threadIdx.x + i * C::NT, row = c / C::CPR_A, k = k0 + (c % C::CPR_A) * 8;
-            const int gm = min(m0 + row, M - 1);
-            ra[i] = (k < K) ? *reinterpret_cast<const v4i*>(X + (int64_t)gm * K + k) : v4i{};
-        }
-#pragma unroll
-        for (int i = 0; i < C::LB; i++) {
-            const int c = threadIdx.x + i * C::NT, row = c / C::CPR_B, k = k0 + (c % C::CPR_B) * C::KPC;
-            const int gn = min(n0 + row, N - 1);
-            const bool in = k < K && c < C::NB;
-            rb[i] = in ? *reinterpret_cast<const v4i*>(Bq + gn * rowbytes + (BITS == 8 ? k : k / 2)) : v4i{};
-            if (BITS == 4) rs[i] = in ? (float)S[(int64_t)gn * G + k / 32] : 0.0f;
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < C::LA; i++) {
-            const int c = threadIdx.x + i * C::NT;
-            *reinterpret_cast<v4i*>(&As[buf][(c / C::CPR_A) * C::LDK + (c % C::CPR_A) * 8]) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::LB; i++) {
-            const int c = threadIdx.x + i * C::NT;
-            if (c >= C::NB) break;
-            half_t* dst = &Bs[buf][(c / C::CPR_B) * C::LDK + (c % C::CPR_B) * C::KPC];
-            if constexpr (BITS == 8) {
-                v8h lo, hi;
-                decode8(rb[i], lo, hi);
-                reinterpret_cast<v8h*>(dst)[0] = lo;
-                reinterpret_cast<v8h*>(dst)[1] = hi;
-            } else {
-                v8h o[4];
-                decode4(rb[i], rs[i], o);
-#pragma unroll
-                for (int q = 0; q < 4; q++) reinterpret_cast<v8h*>(dst)[q] = o[q];
-            }
-        }
-    };
-
-    const int nk = (K + C::BK - 1) / C::BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * C::BK);
-#pragma unroll
-        for (int ks = 0; ks < C::BK / 16; ks++) {
-            v8h a[C::FM], b[C::FN];
-            const int koff = ks * 16 + (lane / 32) * 8;
-#pragma unroll
-            for (int i = 0; i < C::FM; i++)
-                a[i] = *reinterpret_cast<const v8h*>(&As[buf][(wm * C::WTM + i * 32 + lane % 32) * C::LDK + koff]);
-#pragma unroll
-            for (int j = 0; j < C::FN; j++)
-                b[j] = *reinterpret_cast<const v8h*>(&Bs[buf][(wn * C::WTN + j * 32 + lane % 32) * C::LDK + koff]);
-#pragma unroll
-            for (int i = 0; i < C::FM; i++)
-#pragma unroll
-                for (int j = 0; j < C::FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    const float alpha = load_alpha(epi);
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) {
-            const int col = n0 + wn * C::WTN + j * 32 + lane % 32;
-            if (col >= N) continue;
-            const float sc = BITS == 8 ? (float)S[col] : 1.0f;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = m0 + wm * C::WTM + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (row >= M) continue;
-                const int64_t idx = (int64_t)row * N + col;
-                Y[idx] = (half_t)epilogue_apply(acc[i][j][r] * sc, idx, col, epi, alpha);
-            }
-        }
-}
 
 // ---------------------------------------------------------------------------
 // skinny kernel: M <= 16 * MT, 4 waves x 16 output channels, K split over waves
@@ -251,31 +121,21 @@ __global__ __launch_bounds__(256) void gemm_wxa16_skinny_kernel(
 size_t wxa16_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
 
 template <int BITS>
-static hipError_t launch_bits(const half_t* x, const uint8_t* wq, const half_t* s, half_t* y, int M, int N,
-                              int K, const Epi& epi, hipStream_t st) {
-    if (M <= 64) {
-        dim3 grid((N + 15) / 16), block(256);
-        if (M <= 16) hipLaunchKernelGGL((gemm_wxa16_skinny_kernel<BITS, 1>), grid, block, 0, st, x, wq, s, y, M, N, K, epi);
-        else if (M <= 32) hipLaunchKernelGGL((gemm_wxa16_skinny_kernel<BITS, 2>), grid, block, 0, st, x, wq, s, y, M, N, K, epi);
-        else hipLaunchKernelGGL((gemm_wxa16_skinny_kernel<BITS, 4>), grid, block, 0, st, x, wq, s, y, M, N, K, epi);
-    } else if (M <= 512) {
-        constexpr int BM = 64, BN = 64;
-        const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-        hipLaunchKernelGGL((gemm_wxa16_tiled_kernel<BITS, BM, BN, 2, 2>), dim3(tiles), dim3(256), 0, st,
-                           x, wq, s, y, M, N, K, epi);
-    } else {
-        constexpr int BM = 128, BN = 128;
-        const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-        hipLaunchKernelGGL((gemm_wxa16_tiled_kernel<BITS, BM, BN, 2, 2>), dim3(tiles), dim3(256), 0, st,
-                           x, wq, s, y, M, N, K, epi);
-    }
+static hipError_t launch_skinny(const half_t* x, const uint8_t* wq, const half_t* s, half_t* y, int M, int N, int K,
+                                const Epi& epi, hipStream_t st) {
+    dim3 grid((N + 15) / 16), block(256);
+    if (M <= 16) hipLaunchKernelGGL((gemm_wxa16_skinny_kernel<BITS, 1>), grid, block, 0, st, x, wq, s, y, M, N, K, epi);
+    else if (M <= 32) hipLaunchKernelGGL((gemm_wxa16_skinny_kernel<BITS, 2>), grid, block, 0, st, x, wq, s, y, M, N, K, epi);
+    else hipLaunchKernelGGL((gemm_wxa16_skinny_kernel<BITS, 4>), grid, block, 0, st, x, wq, s, y, M, N, K, epi);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_wxa16(int bits, const half_t* x, const void* wq, const half_t* s, half_t* y, int M,
                              int N, int K, const Epi& epi, void*, size_t, hipStream_t st) {
     const uint8_t* w = static_cast<const uint8_t*>(wq);
-    return bits == 8 ? launch_bits<8>(x, w, s, y, M, N, K, epi, st) : launch_bits<4>(x, w, s, y, M, N, K, epi, st);
+    if (M <= 64)
+        return bits == 8 ? launch_skinny<8>(x, w, s, y, M, N, K, epi, st) : launch_skinny<4>(x, w, s, y, M, N, K, epi, st);
+    return launch_gemm_tiled(bits == 8 ? 1 : 2, x, wq, s, nullptr, y, M, N, K, epi, st);
 }
 
 }  // namespace aria

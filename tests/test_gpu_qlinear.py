@@ -235,3 +235,27 @@ def test_w8a8_mlp_up_full_size(q):
     log("w8a8 2048x1536x6144 + GELU")
     out, ref = run_w8a8(q, blk["h"], blk["up"], {"gelu": True}, rows)
     assert_close(out, ref, "w8a8 2048x1536x6144")
+
+
+TILES = ["256x192x4x2", "256x192x2x2", "256x256x4x2", "256x128x4x2", "128x256x2x4", "128x192x2x2",
+         "128x128x2x2", "64x192x2x2", "128x64x2x2", "64x128x2x2", "64x64x2x2"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("mode", ["w8a8", "w8a16", "w4a16"])
+@pytest.mark.parametrize("N", [460, 520])
+def test_every_tile_variant(q, tile, mode, N, monkeypatch):
+    """Every macro-tile variant of the tiled kernel (forced through the tuning
+    override) on ragged shapes that span several tiles and a K tail; N = 460
+    takes the element-wise epilogue (N % 8 != 0), N = 520 the vector one with
+    a partial last tile."""
+    monkeypatch.setenv("ARIA_QLINEAR_TILE", tile)
+    M, K = 300, 352
+    log(f"{mode} tile {tile} {M}x{K}x{N}")
+    x, w = _rand(M, K, N, 4242)
+    e = _epi_inputs(M, N, 9, bias=True, gelu=True, residual=True, steer=True)
+    if mode == "w8a8":
+        out, ref = run_w8a8(q, x, w, e)
+    else:
+        out, ref = run_wxa16(q, 8 if mode == "w8a16" else 4, x, w, e)
+    assert_close(out, ref, f"{mode} {tile}")
