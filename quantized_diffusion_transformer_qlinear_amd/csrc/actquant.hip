@@ -29,7 +29,9 @@ template <int CH>  // CH 16-byte chunks per lane kept in registers (K <= CH * 51
 __global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict__ x, int M, int K,
                                                        int8_t* __restrict__ xq, half_t* __restrict__ sa) {
     const int lane = threadIdx.x % WAVE;
-    const int m = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+    // the row is uniform over the wave; saying so keeps the buffer descriptors
+    // in scalar registers (no per-lane waterfall around each load)
+    const int m = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE);
     if (m >= M) return;
     const rsrc_t rx = make_rsrc(x + (int64_t)m * K, (uint32_t)K * 2);
     const rsrc_t rq = make_rsrc(xq + (int64_t)m * K, (uint32_t)K);
@@ -44,6 +46,7 @@ __global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict_
     a = wave_max(a);
     const half_t sh = (half_t)(a / 127.0f);
     const float s = (float)sh;
+    const float sdiv = s == 0.0f ? 1.0f : s;  // an all-zero row quantizes to zeros either way
     if (lane == 0) sa[m] = sh;
 #pragma unroll
     for (int c = 0; c < CH; c++) {
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict_
             u32 packed = 0;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                float r = (s == 0.0f) ? 0.0f : __builtin_rintf((float)v[c][4 * h + e] / s);
+                float r = __builtin_rintf((float)v[c][4 * h + e] / sdiv);
                 r = fminf(fmaxf(r, -127.0f), 127.0f);
                 packed |= ((u32)(int)r & 0xFFu) << (8 * e);
             }

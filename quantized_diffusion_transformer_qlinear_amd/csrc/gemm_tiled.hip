@@ -21,52 +21,12 @@
 // -> fp16 by building the fp16 pattern 0x6400 | u (= 1024 + u) and
 // subtracting the bias, two values per packed-half instruction.
 #include "common.h"
+#include "decode.h"
 #include "kernels.h"
 
 namespace aria {
 
 namespace {
-
-// 16 int8 (4 dwords) -> 16 fp16, exact: (b ^ 0x80) = q + 128 -> fp16(0x6400 | u) - 1152.
-__device__ __forceinline__ void dec8(v4i w, v4i& lo, v4i& hi) {
-    const v2h bias = {(half_t)1152.0f, (half_t)1152.0f};
-    u32 o[8];
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-        const u32 u = (u32)w[d] ^ 0x80808080u;
-        const u32 p0 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // bytes: u0, 64, u1, 64
-        const u32 p1 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // bytes: u2, 64, u3, 64
-        v2h h0 = __builtin_bit_cast(v2h, p0) - bias;
-        v2h h1 = __builtin_bit_cast(v2h, p1) - bias;
-        o[2 * d] = __builtin_bit_cast(u32, h0);
-        o[2 * d + 1] = __builtin_bit_cast(u32, h1);
-    }
-    lo = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-    hi = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
-}
-
-// 32 nibbles (4 dwords; even k in the low nibble) -> 32 fp16 values fp16(q * s):
-// (n ^ 8) = q + 8 -> fp16(0x6400 | u) - 1032 = q (exact) -> times s (one rounding).
-__device__ __forceinline__ void dec4(v4i w, half_t s, v4i out[4]) {
-    const v2h bias = {(half_t)1032.0f, (half_t)1032.0f};
-    const v2h sc = {s, s};
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-        const u32 u = (u32)w[d] ^ 0x88888888u;
-        const u32 t0 = u & 0x0F0F0F0Fu;          // bytes: k0 k2 k4 k6
-        const u32 t1 = (u >> 4) & 0x0F0F0F0Fu;   // bytes: k1 k3 k5 k7
-        u32 o[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            // k = 2j (byte j of t0) in the low half, k = 2j+1 (byte j of t1) in the high half
-            const u32 sel = 0x0C000C00u | (u32)j | ((u32)(4 + j) << 16);
-            const u32 p = __builtin_amdgcn_perm(t1, t0, sel) | 0x64006400u;
-            v2h h = (__builtin_bit_cast(v2h, p) - bias) * sc;
-            o[j] = __builtin_bit_cast(u32, h);
-        }
-        out[d] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-    }
-}
 
 template <int MODE>
 struct ModeT;
@@ -364,15 +324,22 @@ namespace {
 
 struct TileCfg {
     int bm, bn, wm, wn;
+    float eff[3];  // sustained throughput of one full wave of such tiles, per mode (relative units)
 };
 
-// Candidate macro tiles.  The choice balances CU fill (whole waves of tiles
-// over the CUs) against per-tile efficiency: a wave tile of a x b 32x32 blocks
-// reads (a + b) fragments from LDS for a * b MFMAs, and 8-wave workgroups put
-// two waves on every SIMD so one can issue while the other waits.
+// Candidate macro tiles with their measured per-tile efficiency on MI355X
+// (throughput of a whole number of tile waves at M = 2048, K = 2048, by mode
+// W8A8 / W8A16 / W4A16).  The picker minimises
+//   ceil(tiles / CUs) * BM * BN / eff
+// i.e. it trades CU fill (whole waves of tiles) against per-tile efficiency;
+// 8-wave workgroups put two waves on every SIMD so one can issue while the
+// other waits on LDS or memory.
 constexpr TileCfg kTiles[] = {
-    {256, 192, 4, 2}, {256, 192, 2, 2}, {256, 256, 4, 2}, {256, 128, 4, 2}, {128, 256, 2, 4},
-    {128, 192, 2, 2}, {128, 128, 2, 2}, {64, 192, 2, 2}, {128, 64, 2, 2}, {64, 128, 2, 2}, {64, 64, 2, 2}};
+    {256, 256, 4, 2, {1845.f, 1248.f, 1176.f}}, {256, 192, 4, 2, {1545.f, 970.f, 893.f}},
+    {256, 128, 4, 2, {1599.f, 1015.f, 856.f}},  {128, 256, 2, 4, {1605.f, 1008.f, 899.f}},
+    {128, 192, 2, 2, {1168.f, 744.f, 611.f}},   {128, 128, 2, 2, {1347.f, 795.f, 731.f}},
+    {64, 192, 2, 2, {1211.f, 706.f, 516.f}},    {128, 64, 2, 2, {1160.f, 672.f, 531.f}},
+    {64, 128, 2, 2, {1163.f, 619.f, 559.f}},    {64, 64, 2, 2, {1097.f, 570.f, 358.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -385,7 +352,7 @@ int num_cus() {
     return cus;
 }
 
-TileCfg pick_tile(int M, int N) {
+const TileCfg& pick_tile(int mode, int M, int N) {
     const char* env = getenv("ARIA_QLINEAR_TILE");  // "BMxBNxWMxWN" tuning override
     if (env) {
         int bm = 0, bn = 0, wm = 0, wn = 0;
@@ -395,17 +362,14 @@ TileCfg pick_tile(int M, int N) {
     }
     const int cus = num_cus();
     double best = 1e300;
-    TileCfg pick = kTiles[0];
+    const TileCfg* pick = &kTiles[0];
     for (const TileCfg& t : kTiles) {
-        const double a = t.bm / t.wm / 32.0, b = t.bn / t.wn / 32.0;
-        const double lds_eff = fmin(1.0, 1.5 * (a * b) / (a + b));       // LDS fragment traffic per MFMA
-        const double occ_eff = (t.wm * t.wn >= 8 || t.bm * t.bn <= 128 * 128) ? 1.0 : 0.8;  // latency hiding
         const long tiles = (long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
         const long waves = (tiles + cus - 1) / cus;
-        const double cost = (double)waves * t.bm * t.bn / (lds_eff * occ_eff);
-        if (cost < best) best = cost, pick = t;
+        const double cost = (double)waves * t.bm * t.bn / t.eff[mode];
+        if (cost < best) best = cost, pick = &t;
     }
-    return pick;
+    return *pick;
 }
 
 template <int MODE, int BM, int BN, int WM, int WN>
@@ -418,14 +382,14 @@ hipError_t launch_one(const void* a, const uint8_t* b, const half_t* s, const ha
 }
 
 template <int MODE>
-hipError_t launch_mode(TileCfg t, const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y,
+hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y,
                        int M, int N, int K, const Epi& e, hipStream_t st) {
 #define ARIA_TILE(BM_, BN_, WM_, WN_)                          \
     if (t.bm == BM_ && t.bn == BN_ && t.wm == WM_ && t.wn == WN_) \
         return launch_one<MODE, BM_, BN_, WM_, WN_>(a, b, s, sa, y, M, N, K, e, st);
-    ARIA_TILE(256, 192, 4, 2) ARIA_TILE(256, 192, 2, 2) ARIA_TILE(256, 256, 4, 2) ARIA_TILE(256, 128, 4, 2)
-    ARIA_TILE(128, 256, 2, 4) ARIA_TILE(128, 192, 2, 2) ARIA_TILE(128, 128, 2, 2) ARIA_TILE(64, 192, 2, 2)
-    ARIA_TILE(128, 64, 2, 2) ARIA_TILE(64, 128, 2, 2) ARIA_TILE(64, 64, 2, 2)
+    ARIA_TILE(256, 256, 4, 2) ARIA_TILE(256, 192, 4, 2) ARIA_TILE(256, 128, 4, 2) ARIA_TILE(128, 256, 2, 4)
+    ARIA_TILE(128, 192, 2, 2) ARIA_TILE(128, 128, 2, 2) ARIA_TILE(64, 192, 2, 2) ARIA_TILE(128, 64, 2, 2)
+    ARIA_TILE(64, 128, 2, 2) ARIA_TILE(64, 64, 2, 2)
 #undef ARIA_TILE
     return hipErrorInvalidValue;
 }
@@ -437,7 +401,7 @@ hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half
     // 32-bit buffer offsets: split very tall problems into row blocks
     const int64_t aeb = mode == 0 ? 1 : 2;
     const int64_t max_rows = ((int64_t)1 << 31) / ((int64_t)K * aeb) / 256 * 256;
-    const TileCfg t = pick_tile(M > max_rows ? (int)max_rows : M, N);
+    const TileCfg& t = pick_tile(mode, M > max_rows ? (int)max_rows : M, N);
     const uint8_t* b = static_cast<const uint8_t*>(bq);
     for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
         const int rows = (int)((M - r0) < max_rows ? (M - r0) : max_rows);
