@@ -10,10 +10,16 @@ One step = one pass of the three qlinear modes at M = 2048 tokens, DiT width
   2. W8A16 MLP-up 1536->6144 + bias + GELU;
   3. W4A16 (signed 4-bit, group 32) 1536->6144.
 Weights are packed once before timing (the fp16 copies are then freed).
-The printed value is the aggregate contraction throughput of the step in TOPS
-(2*M*K*N per linear; int8 and fp16 operations counted alike).
+The step is captured once into a HIP graph and the timed region replays it K
+times (the pages replay the denoising loop as one captured graph; the C-ABI
+enqueues without allocating or synchronising, so it captures as-is).  The
+printed value is the aggregate contraction throughput of the step in TOPS
+(2*M*K*N per linear; int8 and fp16 operations counted alike).  A second,
+eager pass times every call with events for the per-call breakdown and the
+dominant kernel's roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--eager] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -29,8 +35,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "qlinear TOPS + % of MFMA/HBM roofline (W8A8, W8A16, W4A16) at M=2048"
 PEAK = {"int8": 5000.0, "fp16": 2500.0, "hbm": 8000.0}  # TOPS, TFLOP/s, GB/s (MI355X datasheet, dense)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["common.h", "gemm_w8a8.hip", "gemm_wxa16.hip", "actquant.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_dit_qlinear_m2048.txt")
+KERNEL_SOURCES = ["common.h", "decode.h", "gemm_tiled.hip", "gemm_skinny.hip", "actquant.hip"]
 
 
 def kernel_hash() -> str:
@@ -51,6 +57,24 @@ def linears(M=2048, W=1536, F=6144):
         ("w8a16.up", "w8a16", W, F, F * 2),                 # + bias
         ("w4a16", "w4a16", W, F, 0),
     ]
+
+
+def read_traffic(call: str):
+    """HBM bytes per launch of `call` measured with rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy's reading), if taken on the current kernels."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for ln in fh:
+                if ":" in ln and not ln.lstrip().startswith("#"):
+                    k, v = ln.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_hash") != kernel_hash():
+            return None
+        v = kv.get(f"bytes_per_launch[{call}]")
+        return float(v) if v is not None else None
+    except (OSError, ValueError):
+        return None
 
 
 def algo_bytes(mode, M, K, N, extra):
@@ -112,6 +136,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the qlinear path is data-parallel over tokens and "
@@ -178,18 +205,58 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    graph = None
+    if not args.eager:
+        # capture one step on a side stream (torch's capture API), then replay it
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step()  # warm the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                step()
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for s in range(args.steps):
-        step(evs[s])
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    per = {n: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps * 1e3
+
+    # eager pass with events between the calls: per-call durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    per = {n: sum(evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)) / args.steps * 1e3
            for i, n in enumerate(names)}  # us per call
+
+    copy_us = None
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_us = c0.elapsed_time(c1) / 5 * 1e3
+        del src, dst
 
     lin = {n: (mode, K, N, extra) for n, mode, K, N, extra in linears()}
     total_ops = sum(2.0 * M * K * N for _, K, N, _ in lin.values())
@@ -212,15 +279,10 @@ def main():
     dom = max((n for n in lin if lin[n][0] != "w8a8"), key=lambda n: per[n])
     mode, K, N, extra = lin[dom]
     rf = roofline(mode, M, K, N, extra, per[dom])
-    rf["kernel"] = f"{dom} ({'gemm_wxa16_tiled_kernel<8,128,128>' if mode == 'w8a16' else 'gemm_wxa16_tiled_kernel<4,128,128>'})"
-    rf["traffic"] = None
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            t = json.load(fh)
-        if t.get("kernel_hash") == kernel_hash() and dom in t.get("per_launch_bytes", {}):
-            rf["traffic"] = t["per_launch_bytes"][dom]
-    except (OSError, ValueError):
-        pass
+    rf["kernel"] = f"{dom} (gemm_tiled_kernel, mode {'W8A16' if mode == 'w8a16' else 'W4A16'})"
+    rf["us_per_launch"] = round(per[dom], 2)
+    rf["algorithmic"] = {"flop": 2.0 * M * K * N, "bytes": algo_bytes(mode, M, K, N, extra)}
+    rf["traffic"] = read_traffic(dom)
     for k in ("achieved", "frac"):
         rf[k] = round(rf[k], 4 if k == "frac" else 1)
 
@@ -234,9 +296,13 @@ def main():
                                "(+bias, GELU) + W4A16 g32 1536x6144",
                    "tokens": M, "width": si.WIDTH, "mlp": si.MLP, "ops_per_step": total_ops},
         "roofline": rf,
+        "timing": "HIP graph replay of the step" if graph is not None else "eager launches",
         "modes": modes,
         "calls": calls,
     }
+    if copy_us is not None:
+        out["copy_calibration"] = {"bytes": 2 * (256 << 20), "us": round(copy_us, 2),
+                                   "GB/s": round(2 * (256 << 20) / copy_us / 1e3, 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
     print(json.dumps(out), flush=True)

@@ -68,9 +68,16 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
 
     __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
 
-    const int ntm = (M + BM - 1) / BM;
+    // Tile order: groups of GM row-blocks, column-major inside a group, after
+    // the XCD remap; the 32 consecutive tiles one XCD runs then form a compact
+    // (GM x 8) block, so its L2 holds GM row-blocks of X instead of all of them.
+    constexpr int GM = 4;
+    const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int tm = bid % ntm, tn = bid / ntm;
+    const int first_m = (bid / (GM * ntn)) * GM;
+    const int gsize = min(ntm - first_m, GM);
+    const int in_group = bid % (GM * ntn);
+    const int tm = first_m + in_group % gsize, tn = in_group / gsize;
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
     const int wm = wave / WN, wn = wave % WN;
