@@ -230,8 +230,26 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     uint32_t* stage = reinterpret_cast<uint32_t*>(&lds[0][0]) + wave * 32 * SROW;
     const float alpha = load_alpha(epi);
     const bool vec_ok = (N % 8) == 0;
+    const v8h zero8 = {};
 #pragma unroll
     for (int i = 0; i < FM; i++) {
+        // 1) issue this round's per-element operand loads (column scales,
+        //    per-row scale, residual) first, so their latency overlaps the
+        //    staging below; bias and d are small, shared by every row and
+        //    cache-resident, so they are read where they are used
+        v8h sw8[TASKS], r8[TASKS];
+        float sr[TASKS];
+#pragma unroll
+        for (int t = 0; t < TASKS; t++) {
+            const int task = lane + t * WAVE, rr = task / CPRW, cc = task % CPRW;
+            const int row = m0 + wm * WTM + i * 32 + rr, col = n0 + wn * WTN + cc * 8;
+            const bool v = vec_ok && row < M && col + 8 <= N;
+            const int64_t base = (int64_t)row * N + col;
+            sw8[t] = (MODE != 2 && v) ? *reinterpret_cast<const v8h*>(S + col) : zero8;
+            sr[t] = (MODE == 0 && v) ? (float)sa[row] : 0.0f;
+            r8[t] = (epi.residual && v) ? *reinterpret_cast<const v8h*>(epi.residual + base) : zero8;
+        }
+        // 2) stage the raw accumulators of block-row i
 #pragma unroll
         for (int j = 0; j < FN; j++)
 #pragma unroll
@@ -243,6 +261,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                 stage[rr * SROW + j * 32 + lane % 32] = __builtin_bit_cast(uint32_t, val);
             }
         __syncthreads();
+        // 3) finish 8 consecutive columns of one row per task
 #pragma unroll
         for (int t = 0; t < TASKS; t++) {
             const int task = lane + t * WAVE, rr = task / CPRW, cc = task % CPRW;
@@ -253,23 +272,19 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
             uint32_t raw[8];
 #pragma unroll
             for (int e = 0; e < 8; e++) raw[e] = stage[rr * SROW + cc * 8 + e];
-            const v4u lo = {raw[0], raw[1], raw[2], raw[3]}, hi = {raw[4], raw[5], raw[6], raw[7]};
             const int64_t base = (int64_t)row * N + col;
             if (vec_ok && col + 8 <= N) {
                 float v[8];
                 if constexpr (MODE == 0) {
                     if (epi.acc_out) {
-                        reinterpret_cast<v4u*>(epi.acc_out + base)[0] = lo;
-                        reinterpret_cast<v4u*>(epi.acc_out + base)[1] = hi;
+                        reinterpret_cast<v4u*>(epi.acc_out + base)[0] = v4u{raw[0], raw[1], raw[2], raw[3]};
+                        reinterpret_cast<v4u*>(epi.acc_out + base)[1] = v4u{raw[4], raw[5], raw[6], raw[7]};
                     }
-                    const float sr = (float)sa[row];
-                    const v8h sw8 = *reinterpret_cast<const v8h*>(S + col);
 #pragma unroll
-                    for (int e = 0; e < 8; e++) v[e] = (float)(int32_t)raw[e] * sr * (float)sw8[e];
+                    for (int e = 0; e < 8; e++) v[e] = (float)(int32_t)raw[e] * sr[t] * (float)sw8[t][e];
                 } else if constexpr (MODE == 1) {
-                    const v8h sw8 = *reinterpret_cast<const v8h*>(S + col);
 #pragma unroll
-                    for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]) * (float)sw8[e];
+                    for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]) * (float)sw8[t][e];
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]);
@@ -284,9 +299,8 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                     for (int e = 0; e < 8; e++) v[e] = gelu_tanh(v[e]);
                 }
                 if (epi.residual) {
-                    const v8h r8 = *reinterpret_cast<const v8h*>(epi.residual + base);
 #pragma unroll
-                    for (int e = 0; e < 8; e++) v[e] += (float)r8[e];
+                    for (int e = 0; e < 8; e++) v[e] += (float)r8[t][e];
                 }
                 if (alpha != 0.0f) {
                     const v4f d0 = *reinterpret_cast<const v4f*>(epi.steer_dir + col);
