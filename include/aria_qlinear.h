@@ -34,8 +34,10 @@
  *     error nothing is launched and a negative aria_status is returned.  A
  *     failed launch returns ARIA_E_HIP.  Errors inside a kernel surface at the
  *     caller's next synchronisation.  Inputs must be finite.
- *   - Shapes: M tokens, K inputs, N outputs; M, N >= 1, K >= 32 and
- *     K % 32 == 0.  Every pointer must be 16-byte aligned.
+ *   - Shapes: M tokens, K inputs, N outputs; 1 <= M <= 2^30,
+ *     1 <= N <= 2^30, 32 <= K <= 16384, K % 32 == 0 and N * K < 2^31 (the
+ *     packed weights of one layer are addressed with 32-bit offsets).  Every
+ *     pointer must be 16-byte aligned.
  *   - Layouts (row-major):
  *       X   fp16 [M][K]            activations
  *       W   fp16 [K][N]            unpacked weights (input of aria_qpack only)

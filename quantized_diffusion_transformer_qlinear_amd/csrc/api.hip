@@ -65,7 +65,7 @@ const char* aria_status_string(int s) {
     switch (s) {
         case ARIA_OK: return "ok";
         case ARIA_E_NULL: return "a required pointer is NULL";
-        case ARIA_E_SHAPE: return "M, K or N out of range (M, N >= 1; 32 <= K <= 16384; K % 32 == 0)";
+        case ARIA_E_SHAPE: return "M, K or N out of range (1 <= M <= 2^30; 1 <= N <= 2^30; 32 <= K <= 16384; K % 32 == 0; N * K < 2^31)";
         case ARIA_E_ALIGN: return "a pointer is not 16-byte aligned";
         case ARIA_E_UNSUPPORTED: return "unsupported bits/group/epilogue option";
         case ARIA_E_WORKSPACE: return "workspace missing or too small";

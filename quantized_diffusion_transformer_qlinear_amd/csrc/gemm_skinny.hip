@@ -22,14 +22,6 @@
 
 namespace aria {
 
-namespace {
-
-__device__ __forceinline__ half_t buf_load_h(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
-}
-
-}  // namespace
-
 template <int BITS, int MT, int CG, int NS>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(const half_t* __restrict__ X, const uint8_t* __restrict__ Bq,
                                                           const half_t* __restrict__ S, half_t* Y, int M, int N,

@@ -190,28 +190,6 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
             store_part(cur ^ 1, p);
             load_part(kt + 2, p);
         }
-#if defined(ARIA_SCHED) && ARIA_SCHED == 1
-        __builtin_amdgcn_iglp_opt(0);
-#elif defined(ARIA_SCHED) && ARIA_SCHED == 2
-        __builtin_amdgcn_iglp_opt(1);
-#elif defined(ARIA_SCHED) && ARIA_SCHED == 3
-        {
-            constexpr int NMF = FM * FN;
-            constexpr int NW = LA + LB * (MODE == 0 ? 1 : (MODE == 1 ? 2 : 4));   // ds_write per K-step
-            constexpr int NL = LA + LB;                                            // buffer loads per K-step
-            __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-#pragma unroll
-            for (int sp = 0; sp < 4; sp++)
-#pragma unroll
-                for (int m = 0; m < NMF; m++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (sp < 3 && m < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, MODE == 2 ? 3 : 2, 0);
-                    if ((sp * NMF + m) % ((4 * NMF + NW - 1) / NW) == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-                    if ((sp * NMF + m) % ((4 * NMF + NL - 1) / NL) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                }
-        }
-#endif
         __syncthreads();
     }
 
@@ -260,7 +238,11 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                 const auto val = acc[i][j][r];
                 stage[rr * SROW + j * 32 + lane % 32] = __builtin_bit_cast(uint32_t, val);
             }
-        __syncthreads();
+        // the slice is this wave's own: LDS executes one wave's accesses in
+        // order, so a wavefront-scope fence (which keeps the compiler from
+        // reordering) is all the staging needs; a workgroup barrier would
+        // also wait for this wave's outstanding global stores
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         // 3) finish 8 consecutive columns of one row per task
 #pragma unroll
         for (int t = 0; t < TASKS; t++) {
@@ -334,7 +316,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                 }
             }
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // before the next round restages the slice
     }
 }
 

@@ -71,7 +71,8 @@ def test_validation_codes(q):
     assert _w8a8(q, wq=None) == -1
     assert _w8a8(q, y=None) == -1
     # shapes
-    for M, K, N in ((0, 256, 256), (64, 0, 256), (64, 256, 0), (64, 48, 256), (64, 32768, 256)):
+    for M, K, N in ((0, 256, 256), (64, 0, 256), (64, 256, 0), (64, 48, 256), (64, 32768, 256),
+                    (64, 32, 1 << 26), ((1 << 30) + 1, 256, 256)):
         assert _w8a8(q, X, M, K, N, W, S, None, Y, WS, big) == -2, (M, K, N)
     # alignment
     assert _w8a8(q, X + 2, 64, 256, 256, W, S, None, Y, WS, big) == -3
