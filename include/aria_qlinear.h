@@ -69,7 +69,7 @@ enum aria_status {
     ARIA_E_UNSUPPORTED = -4, /* bits not in {4, 8}, or group not 0 (8-bit) / 32 (4-bit) */
     ARIA_E_WORKSPACE = -5,   /* workspace missing or smaller than required         */
     ARIA_E_HIP = -6,         /* the HIP runtime reported an error at launch        */
-    ARIA_E_ALIAS = -7        /* x overlaps y                                       */
+    ARIA_E_ALIAS = -7        /* an output overlaps an input or another output      */
 };
 
 enum aria_mode { ARIA_W8A8 = 0, ARIA_W8A16 = 1, ARIA_W4A16 = 2 };
@@ -141,6 +141,32 @@ int aria_qlinear_w4a16(const void* x_f16, int64_t M, int64_t K, int64_t N,
                        const uint8_t* wq4, const void* s_g_f16, int group,
                        const aria_epilogue* epi, void* y_f16, void* ws, size_t ws_bytes,
                        aria_stream_t stream);
+
+/* One weight-only linear of a grouped call: Y = epilogue(X * dequant(Wq)) as in
+ * aria_qlinear_w8a16 / aria_qlinear_w4a16.  epi is a host pointer or NULL
+ * (acc_out must be NULL). */
+typedef struct aria_linear_problem {
+    const void* x_f16;        /* X fp16 [M][K]                                             */
+    int64_t M, K, N;
+    const void* wq;           /* Wq int8 [N][K] (bits 8) or Wq4 uint8 [N][K/2] (bits 4)    */
+    const void* s_f16;        /* s_w fp16 [N] (bits 8) or s_g fp16 [N][K/32] (bits 4)      */
+    const aria_epilogue* epi; /* or NULL                                                   */
+    void* y_f16;              /* Y fp16 [M][N]                                             */
+} aria_linear_problem;
+
+/* Several independent weight-only linears at small M in as few launches as
+ * possible (one per 16 problems): the small-M regime of the 4-bit weights is
+ * bound by streaming them from memory (project page, "Results": 4-bit weights
+ * for small devices), and one launch per layer leaves it bound by launch cost
+ * instead.  bits 8 / group 0 runs W8A16, bits 4 / group 32 runs W4A16.
+ * Every problem is checked as the single call checks it, and in addition
+ * 1 <= count <= 1024 (else ARIA_E_SHAPE) and M <= 64 (else ARIA_E_UNSUPPORTED).
+ * The problems run concurrently, so no problem's y may overlap another
+ * problem's x, weights, scales, bias, residual, d or y (ARIA_E_ALIAS).
+ * `problems` is a host array, read only during the call.  Results are
+ * bit-identical to one aria_qlinear_w8a16 / aria_qlinear_w4a16 call per problem. */
+int aria_qlinear_grouped(int bits, int group, const aria_linear_problem* problems, int count,
+                         aria_stream_t stream);
 
 #ifdef __cplusplus
 }

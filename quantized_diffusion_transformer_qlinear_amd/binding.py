@@ -43,6 +43,15 @@ lib.aria_qlinear_w4a16.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I, ctypes.POIN
 lib.aria_qlinear_w4a16.restype = _I
 
 
+class LinearProblem(ctypes.Structure):
+    _fields_ = [("x_f16", _P), ("M", _I64), ("K", _I64), ("N", _I64), ("wq", _P), ("s_f16", _P),
+                ("epi", ctypes.POINTER(Epilogue)), ("y_f16", _P)]
+
+
+lib.aria_qlinear_grouped.argtypes = [_I, _I, ctypes.POINTER(LinearProblem), _I, _P]
+lib.aria_qlinear_grouped.restype = _I
+
+
 class AriaError(RuntimeError):
     def __init__(self, code: int, what: str):
         super().__init__(f"{what}: {status_string(code)} ({code})")
@@ -184,3 +193,28 @@ def qlinear_w4a16(x, wq4, sg, y=None, ws=None, bias=None, gelu=False, residual=N
     _check(lib.aria_qlinear_w4a16(_addr(x), M, K, N, _addr(wq4), _addr(sg), group, ctypes.byref(e), _addr(y),
                                   _addr(ws), nb, _stream(stream)), "qlinear_w4a16")
     return y
+
+
+def qlinear_grouped(bits: int, problems, stream=None):
+    """Several independent weight-only linears at small M in one call.
+    ``problems``: a list of dicts with keys x, wq, s and optionally y, bias,
+    gelu, residual, steer_dir, steer_alpha (as for qlinear_w8a16 /
+    qlinear_w4a16).  bits 8 -> W8A16, bits 4 -> W4A16 (group 32).  Returns the
+    list of outputs."""
+    torch = _torch()
+    arr = (LinearProblem * len(problems))()
+    keep, outs = [], []
+    for i, p in enumerate(problems):
+        x, wq, s = p["x"], p["wq"], p["s"]
+        _dt(x, torch.float16, "x"), _dt(wq, torch.int8 if bits == 8 else torch.uint8, "wq"), _dt(s, torch.float16, "s")
+        M, K = x.shape
+        N = wq.shape[0]
+        y = _out(x, N, p.get("y"))
+        e = _epi(p.get("bias"), p.get("gelu", False), p.get("residual"), p.get("steer_dir"),
+                 p.get("steer_alpha"), None)
+        keep.append(e)
+        outs.append(y)
+        arr[i] = LinearProblem(_addr(x), M, K, N, _addr(wq), _addr(s), ctypes.pointer(e), _addr(y))
+    _check(lib.aria_qlinear_grouped(bits, 0 if bits == 8 else 32, arr, len(problems), _stream(stream)),
+           "qlinear_grouped")
+    return outs

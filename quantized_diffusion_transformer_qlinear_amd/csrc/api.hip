@@ -13,6 +13,8 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // M and N limits (int indexing in kernels)
 constexpr int64_t kMaxK = 16384;                 // activation-quant keeps a row in registers
 constexpr size_t kAlign = 256;                    // workspace sub-buffer alignment
+constexpr int kGroupedMax = 1024;                 // problems per grouped call
+constexpr int64_t kGroupedMaxM = 64;              // the grouped path is the small-M kernel
 
 inline bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
@@ -175,6 +177,65 @@ int aria_qlinear_w4a16(const void* x, int64_t M, int64_t K, int64_t N, const uin
                        aria_stream_t stream) {
     if (group != 32) return ARIA_E_UNSUPPORTED;
     return wxa16(4, x, M, K, N, wq4, sg, epi, y, ws, ws_bytes, stream);
+}
+
+int aria_qlinear_grouped(int bits, int group, const aria_linear_problem* problems, int count,
+                         aria_stream_t stream) {
+    if (!((bits == 8 && group == 0) || (bits == 4 && group == 32))) return ARIA_E_UNSUPPORTED;
+    if (!problems) return ARIA_E_NULL;
+    if (count < 1 || count > kGroupedMax) return ARIA_E_SHAPE;
+    const int mode = bits == 8 ? ARIA_W8A16 : ARIA_W4A16;
+    // every problem on its own, as the single call checks it
+    for (int i = 0; i < count; i++) {
+        const aria_linear_problem& p = problems[i];
+        int rc = check_shape(p.M, p.K, p.N);
+        if (rc != ARIA_OK) return rc;
+        if (p.M > kGroupedMaxM) return ARIA_E_UNSUPPORTED;
+        if (!p.x_f16 || !p.wq || !p.s_f16 || !p.y_f16) return ARIA_E_NULL;
+        if (!aligned16(p.x_f16) || !aligned16(p.wq) || !aligned16(p.s_f16) || !aligned16(p.y_f16)) return ARIA_E_ALIGN;
+        if (overlap(p.x_f16, (size_t)(p.M * p.K) * 2, p.y_f16, (size_t)(p.M * p.N) * 2)) return ARIA_E_ALIAS;
+        if (p.epi && p.epi->acc_out) return ARIA_E_UNSUPPORTED;
+        Epi e;
+        if ((rc = make_epi(p.epi, mode, p.M, p.N, p.y_f16, &e)) != ARIA_OK) return rc;
+    }
+    // the problems run concurrently: no output may touch another problem's buffers
+    for (int i = 0; i < count; i++) {
+        const aria_linear_problem& p = problems[i];
+        const size_t yb = (size_t)(p.M * p.N) * 2;
+        for (int j = 0; j < count; j++) {
+            if (j == i) continue;
+            const aria_linear_problem& q = problems[j];
+            const size_t wb = bits == 8 ? (size_t)(q.N * q.K) : (size_t)(q.N * q.K) / 2;
+            const size_t sb = bits == 8 ? (size_t)q.N * 2 : (size_t)q.N * (size_t)(q.K / 32) * 2;
+            const size_t qy = (size_t)(q.M * q.N) * 2;
+            if (overlap(p.y_f16, yb, q.x_f16, (size_t)(q.M * q.K) * 2) || overlap(p.y_f16, yb, q.wq, wb) ||
+                overlap(p.y_f16, yb, q.s_f16, sb) || overlap(p.y_f16, yb, q.y_f16, qy))
+                return ARIA_E_ALIAS;
+            if (q.epi && ((q.epi->bias && overlap(p.y_f16, yb, q.epi->bias, (size_t)q.N * 2)) ||
+                          (q.epi->residual && overlap(p.y_f16, yb, q.epi->residual, qy)) ||
+                          (q.epi->steer_dir && overlap(p.y_f16, yb, q.epi->steer_dir, (size_t)q.N * 4))))
+                return ARIA_E_ALIAS;
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    for (int c0 = 0; c0 < count; c0 += kSkinnyGroupMax) {
+        SkinnyGroup g{};
+        g.count = count - c0 < kSkinnyGroupMax ? count - c0 : kSkinnyGroupMax;
+        for (int i = 0; i < g.count; i++) {
+            const aria_linear_problem& p = problems[c0 + i];
+            SkinnyProblem& d = g.p[i];
+            d.x = static_cast<const half_t*>(p.x_f16);
+            d.w = static_cast<const uint8_t*>(p.wq);
+            d.s = static_cast<const half_t*>(p.s_f16);
+            d.y = static_cast<half_t*>(p.y_f16);
+            make_epi(p.epi, mode, p.M, p.N, p.y_f16, &d.epi);
+            d.M = (int)p.M, d.N = (int)p.N, d.K = (int)p.K;
+        }
+        const int rc = hip_status(launch_skinny_grouped(bits, g, st));
+        if (rc != ARIA_OK) return rc;
+    }
+    return ARIA_OK;
 }
 
 }  // extern "C"

@@ -69,6 +69,12 @@ __device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ half_t buf_load_h(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
 }
+// LDS-DMA: every lane's 16 bytes go straight from the buffer into LDS, lane l
+// to lds_base + 16 l (`lds_base` is one address for the whole wave); an
+// out-of-range lane writes zeros.  Counts as a vector memory load.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t off, char* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
+}
 __device__ __forceinline__ void buf_store8(v2u v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }

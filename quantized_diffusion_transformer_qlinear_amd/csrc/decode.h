@@ -29,9 +29,9 @@ __device__ __forceinline__ void dec8(v4i w, v4i& lo, v4i& hi) {
 
 // 32 nibbles (4 dwords; even k in the low nibble) -> 32 fp16 values fp16(q * s):
 // (n ^ 8) = q + 8 -> fp16(0x6400 | u) - 1032 = q (exact) -> times s (one rounding).
-__device__ __forceinline__ void dec4(v4i w, half_t s, v4i out[4]) {
+// `sc` holds the group scale in both halves.
+__device__ __forceinline__ void dec4(v4i w, v2h sc, v4i out[4]) {
     const v2h bias = {(half_t)1032.0f, (half_t)1032.0f};
-    const v2h sc = {s, s};
 #pragma unroll
     for (int d = 0; d < 4; d++) {
         const u32 u = (u32)w[d] ^ 0x88888888u;
@@ -48,6 +48,13 @@ __device__ __forceinline__ void dec4(v4i w, half_t s, v4i out[4]) {
         }
         out[d] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     }
+}
+__device__ __forceinline__ void dec4(v4i w, half_t s, v4i out[4]) { dec4(w, v2h{s, s}, out); }
+// ... with the scale given as its 16 bits in the low half of a dword (as a
+// 16-bit buffer load returns it): kept in a dword, a scale array stays in
+// registers.
+__device__ __forceinline__ void dec4_bits(v4i w, u32 sbits, v4i out[4]) {
+    dec4(w, __builtin_bit_cast(v2h, (sbits & 0xFFFFu) * 0x10001u), out);
 }
 
 }  // namespace aria

@@ -22,4 +22,24 @@ hipError_t launch_gemm_wxa16(int bits, const half_t* x, const void* wq, const ha
                              hipStream_t st);
 size_t wxa16_workspace_bytes(int bits, int64_t M, int64_t K, int64_t N);
 
+// Grouped weight-only linears at small M (M <= 64): one launch for up to
+// kSkinnyGroupMax problems, each problem's workgroups a slice of one grid.
+// The problem table travels as the kernel argument (no device memory); the
+// launcher fills in `first`.
+constexpr int kSkinnyGroupMax = 16;
+struct SkinnyProblem {
+    const half_t* x;
+    const uint8_t* w;
+    const half_t* s;
+    half_t* y;
+    Epi epi;
+    int M, N, K;
+    int first;  // first workgroup of this problem (set by the launcher)
+};
+struct SkinnyGroup {
+    SkinnyProblem p[kSkinnyGroupMax];
+    int count;
+};
+hipError_t launch_skinny_grouped(int bits, SkinnyGroup& g, hipStream_t st);
+
 }  // namespace aria

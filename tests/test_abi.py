@@ -29,7 +29,7 @@ def q():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (aria_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -106,3 +106,32 @@ def test_validation_codes(q):
     assert L.aria_quant_act(X, 64, 64, None, S, None) == -1
     assert L.aria_qlinear_workspace_bytes(9, 64, 64, 64) == 0
     assert L.aria_qlinear_workspace_bytes(0, 64, 40, 64) == 0
+
+
+def test_grouped_validation_codes(q):
+    L = q.lib
+    P = q.binding.LinearProblem
+    E = q.binding.Epilogue
+    X, W, S, Y = 1 << 20, 2 << 20, 3 << 20, 4 << 20  # never dereferenced
+
+    def call(bits, group, probs):
+        arr = (P * max(len(probs), 1))(*probs)
+        return L.aria_qlinear_grouped(bits, group, arr, len(probs), None)
+
+    ok = P(X, 16, 256, 128, W, S, None, Y)   # valid on its own; every call below fails validation
+    assert call(4, 16, [ok]) == -4 and call(8, 32, [ok]) == -4 and call(3, 0, [ok]) == -4
+    assert L.aria_qlinear_grouped(4, 32, None, 1, None) == -1
+    assert call(4, 32, []) == -2
+    assert call(4, 32, [P(X, 65, 256, 128, W, S, None, Y)]) == -4           # M > 64: not the small-M path
+    assert call(4, 32, [P(X, 16, 48, 128, W, S, None, Y)]) == -2            # K % 32
+    assert call(4, 32, [P(None, 16, 256, 128, W, S, None, Y)]) == -1
+    assert call(4, 32, [P(X + 2, 16, 256, 128, W, S, None, Y)]) == -3
+    assert call(4, 32, [P(X, 16, 256, 128, W, S, None, X + 64)]) == -7      # own x / y overlap
+    ep = E(None, 0, 0, None, None, None, 6 << 20)
+    assert call(4, 32, [P(X, 16, 256, 128, W, S, ctypes.pointer(ep), Y)]) == -4   # acc_out
+    # across problems: y of one may not overlap x, weights, scales or y of another
+    Y2 = 8 << 20
+    assert call(4, 32, [P(X, 16, 256, 128, W, S, None, Y), P(Y, 16, 256, 128, W, S, None, Y2)]) == -7
+    assert call(4, 32, [P(X, 16, 256, 128, W, S, None, Y), P(X, 16, 256, 128, Y + 64, S, None, Y2)]) == -7
+    assert call(4, 32, [P(X, 16, 256, 128, W, S, None, Y), P(X, 16, 256, 128, W, S, None, Y + 2048)]) == -7
+    assert call(8, 0, [P(X, 16, 256, 128, W, S, None, Y)] * 1025) == -2
