@@ -78,6 +78,8 @@ def _load():
             "or_gemm_i8": [P, P, I64, I64, I64, P],
             "or_ref_w8a16": [P, P, P, I64, I64, I64, P],
             "or_ref_w4a16": [P, P, P, I64, I64, I64, I64, P],
+            "or_pack16": [P, I64, I64, P],
+            "or_ref_w16a16": [P, P, I64, I64, I64, P],
             "or_scale_w8a8": [P, P, P, I64, I64, P],
             "or_epilogue": [P, I64, I64, P, ctypes.c_int, P, P, ctypes.c_float],
         }
@@ -230,6 +232,26 @@ def ref_w4a16(x, q4, s4, group: int = 32) -> np.ndarray:
     return r
 
 
+def pack16(w):
+    """W fp16 [K][N] -> Wt fp16 [N][K] (the fp16 rung's weight layout)."""
+    w = _bits(w)
+    K, N = w.shape
+    wt = np.empty((N, K), np.uint16)
+    _check(_load().or_pack16(_ptr(w), K, N, _ptr(wt)), "pack16")
+    return wt.view(np.float16)
+
+
+def ref_w16a16(x, wt) -> np.ndarray:
+    x = _bits(x)
+    wt = _bits(wt)
+    M, K = x.shape
+    N = wt.shape[0]
+    assert wt.shape[1] == K
+    r = np.empty((M, N), np.float64)
+    _check(_load().or_ref_w16a16(_ptr(x), _ptr(wt), M, N, K, _ptr(r)), "ref_w16a16")
+    return r
+
+
 def scale_w8a8(acc, sa, sw) -> np.ndarray:
     acc = _c(acc, np.int32)
     sa = _bits(sa)
@@ -272,6 +294,10 @@ def qlinear_w8a8(x, wq, sw, **epi):
 
 def qlinear_w8a16(x, wq, sw, **epi) -> np.ndarray:
     return epilogue(ref_w8a16(x, wq, sw), **epi)
+
+
+def qlinear_w16a16(x, wt, **epi) -> np.ndarray:
+    return epilogue(ref_w16a16(x, wt), **epi)
 
 
 def qlinear_w4a16(x, q4, s4, group=32, **epi) -> np.ndarray:

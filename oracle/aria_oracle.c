@@ -266,6 +266,36 @@ int or_ref_w4a16(const uint16_t* x, const uint8_t* wq4, const uint16_t* sg, int6
     return 0;
 }
 
+/* The fp16 rung of the precision ladder ([P4] "Results", table "Quantization
+ * is close to free at 8-bit": fp16 is the row the quantized modes are timed
+ * against).  Weights are kept as fp16, laid out like the packed ones: row n
+ * holds column n of W, contiguous along K.  wt[n][k] = w[k][n] (a copy). */
+int or_pack16(const uint16_t* w, int64_t K, int64_t N, uint16_t* wt)
+{
+    if (!w || !wt || K <= 0 || N <= 0) return -1;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) wt[n * K + k] = w[k * N + n];
+    return 0;
+}
+
+/* W16A16: r[m][n] = sum_k x[m][k] * wt[n][k]   (fp64). */
+int or_ref_w16a16(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t N, int64_t K, double* r)
+{
+    if (!x || !wt || !r || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        double* xr = (double*)malloc((size_t)K * sizeof(double));
+        for (int64_t k = 0; k < K; k++) xr[k] = or_f16_to_f64(x[m * K + k]);
+        for (int64_t n = 0; n < N; n++) {
+            double t = 0.0;
+            for (int64_t k = 0; k < K; k++) t += xr[k] * or_f16_to_f64(wt[n * K + k]);
+            r[m * N + n] = t;
+        }
+        free(xr);
+    }
+    return 0;
+}
+
 /* W8A8 dequantization of the accumulator: y[m][n] = acc[m][n] * s_a[m] * s_w[n]. */
 int or_scale_w8a8(const int32_t* acc, const uint16_t* sa, const uint16_t* sw,
                   int64_t M, int64_t N, double* y)

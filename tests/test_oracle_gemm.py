@@ -92,3 +92,48 @@ def test_w8a8_scale_closed_form():
     y = oracle.scale_w8a8(acc, s, np.repeat(s, 3))
     assert y[0, 0] == 0.99993896484375 ** 2
     assert y[0, 1] == -(0.00787353515625 ** 2) and y[0, 2] == 0.0
+
+
+# ---- the fp16 rung (W16A16) ----------------------------------------------
+
+def test_pack16_is_the_transpose():
+    rng = np.random.default_rng(31)
+    w = rng.standard_normal((96, 40)).astype(np.float16)
+    wt = oracle.pack16(w)
+    assert wt.shape == (40, 96) and wt.dtype == np.float16
+    assert np.array_equal(wt.view(np.uint16), np.ascontiguousarray(w.T).view(np.uint16))
+
+
+def test_w16a16_exact_integers():
+    """Small integer-valued fp16 operands: every product and partial sum is an
+    exact integer in fp64, so the reference equals Python integer sums."""
+    rng = np.random.default_rng(32)
+    M, K, N = 7, 96, 11
+    x = rng.integers(-20, 21, (M, K))
+    w = rng.integers(-20, 21, (K, N))
+    r = oracle.ref_w16a16(x.astype(np.float16), oracle.pack16(w.astype(np.float16)))
+    for m in range(M):
+        for n in range(N):
+            assert r[m, n] == sum(int(x[m, k]) * int(w[k, n]) for k in range(K))
+
+
+def test_w16a16_vs_blas():
+    rng = np.random.default_rng(33)
+    M, K, N = 21, 224, 45
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (rng.standard_normal((K, N)) * 0.05).astype(np.float16)
+    r = oracle.ref_w16a16(x, oracle.pack16(w))
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    assert np.max(np.abs(r - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_w16a16_permutation_weights():
+    """A permutation matrix as W selects input columns: y = x[:, perm] exactly."""
+    rng = np.random.default_rng(34)
+    K = 64
+    perm = rng.permutation(K)
+    w = np.zeros((K, K), np.float16)
+    w[perm, np.arange(K)] = 1.0
+    x = rng.standard_normal((9, K)).astype(np.float16)
+    r = oracle.ref_w16a16(x, oracle.pack16(w))
+    assert np.array_equal(r, x.astype(np.float64)[:, perm])

@@ -43,6 +43,8 @@ MUTANTS = {
                         "if (gelu) v = or_gelu_tanh(v);\n            if (bias) v += or_f16_to_f64(bias[n]);"),
     "steer_sign": ("v += (double)alpha * (double)d[n];", "v -= (double)alpha * (double)d[n];"),
     "steer_always": ("if (d && alpha != 0.0f)", "if (d)"),
+    "pack16_not_transposed": ("wt[n * K + k] = w[k * N + n];", "wt[n * K + k] = w[n * K + k];"),
+    "w16a16_row_stride": ("t += xr[k] * or_f16_to_f64(wt[n * K + k]);", "t += xr[k] * or_f16_to_f64(wt[k * N + n]);"),
 }
 
 
