@@ -47,6 +47,7 @@
  *                                  k = 2j in its low nibble, k = 2j+1 in its
  *                                  high nibble, two's complement
  *       s_g fp16 [N][K/32]         4-bit group scales, group g = k in [32g, 32g+32)
+ *       Wt  fp16 [N][K]            fp16 weights (the unquantized rung), row n = column n of W
  *       Y   fp16 [M][N]            output
  */
 #ifndef ARIA_QLINEAR_H
@@ -66,13 +67,13 @@ enum aria_status {
     ARIA_E_NULL = -1,        /* a required pointer is NULL                         */
     ARIA_E_SHAPE = -2,       /* M, K or N out of range, or K % 32 != 0             */
     ARIA_E_ALIGN = -3,       /* a pointer is not 16-byte aligned                   */
-    ARIA_E_UNSUPPORTED = -4, /* bits not in {4, 8}, or group not 0 (8-bit) / 32 (4-bit) */
+    ARIA_E_UNSUPPORTED = -4, /* bits not in {4, 8, 16}, group not 0 (8, 16) / 32 (4), or an option the call lacks */
     ARIA_E_WORKSPACE = -5,   /* workspace missing or smaller than required         */
     ARIA_E_HIP = -6,         /* the HIP runtime reported an error at launch        */
     ARIA_E_ALIAS = -7        /* an output overlaps an input or another output      */
 };
 
-enum aria_mode { ARIA_W8A8 = 0, ARIA_W8A16 = 1, ARIA_W4A16 = 2 };
+enum aria_mode { ARIA_W8A8 = 0, ARIA_W8A16 = 1, ARIA_W4A16 = 2, ARIA_W16A16 = 3 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* aria_status_string(int status);
@@ -83,14 +84,17 @@ int aria_abi_version(void);
 /* Host-only: bytes of the packed weights and of their scales.
  *   bits 8, group 0 : q = K*N, s = 2*N
  *   bits 4, group 32: q = K*N/2, s = 2*N*(K/32)
+ *   bits 16, group 0: q = 2*K*N, s = 0 (the fp16 rung; needs K*N < 2^30)
  * q_bytes / s_bytes are host pointers. */
 int aria_qpack_bytes(int bits, int group, int64_t K, int64_t N, size_t* q_bytes, size_t* s_bytes);
 
 /* a1 — pack fp16 weights W [K][N] (project page, "What aria is": weights from
  * fp16 down to 8 or 4 bits).  bits 8 / group 0 -> Wq int8 [N][K] + s_w fp16 [N];
- * bits 4 / group 32 -> Wq4 uint8 [N][K/2] + s_g fp16 [N][K/32].  q_out and
- * s_out must hold aria_qpack_bytes() bytes.  Once the call has completed on the
- * stream the caller may free W: nothing later reads it. */
+ * bits 4 / group 32 -> Wq4 uint8 [N][K/2] + s_g fp16 [N][K/32]; bits 16 /
+ * group 0 -> Wt fp16 [N][K], the unquantized weights in the same row layout
+ * (s_out unused, may be NULL).  q_out and s_out must hold aria_qpack_bytes()
+ * bytes.  Once the call has completed on the stream the caller may free W:
+ * nothing later reads it. */
 int aria_qpack(int bits, int group, const void* w_f16, int64_t K, int64_t N,
                void* q_out, void* s_out, aria_stream_t stream);
 
@@ -141,6 +145,15 @@ int aria_qlinear_w4a16(const void* x_f16, int64_t M, int64_t K, int64_t N,
                        const uint8_t* wq4, const void* s_g_f16, int group,
                        const aria_epilogue* epi, void* y_f16, void* ws, size_t ws_bytes,
                        aria_stream_t stream);
+
+/* The fp16 rung (project page, "Results", table "Quantization is close to
+ * free at 8-bit": fp16 is the row the quantized modes are timed against):
+ * Y = epilogue( sum_k X[m][k] * Wt[n][k] ) with fp32 accumulation, Wt from
+ * aria_qpack(16, 0, ...).  Same conventions and epilogue as the other modes;
+ * K*N < 2^30. */
+int aria_qlinear_w16a16(const void* x_f16, int64_t M, int64_t K, int64_t N, const void* wt_f16,
+                        const aria_epilogue* epi, void* y_f16, void* ws, size_t ws_bytes,
+                        aria_stream_t stream);
 
 /* One weight-only linear of a grouped call: Y = epilogue(X * dequant(Wq)) as in
  * aria_qlinear_w8a16 / aria_qlinear_w4a16.  epi is a host pointer or NULL

@@ -15,7 +15,7 @@ if not os.path.exists(library_path):
 
 lib = ctypes.CDLL(library_path)
 
-ARIA_W8A8, ARIA_W8A16, ARIA_W4A16 = 0, 1, 2
+ARIA_W8A8, ARIA_W8A16, ARIA_W4A16, ARIA_W16A16 = 0, 1, 2, 3
 _P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
 
 
@@ -41,6 +41,8 @@ for _name in ("aria_qlinear_w8a8", "aria_qlinear_w8a16"):
     getattr(lib, _name).restype = _I
 lib.aria_qlinear_w4a16.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P]
 lib.aria_qlinear_w4a16.restype = _I
+lib.aria_qlinear_w16a16.argtypes = [_P, _I64, _I64, _I64, _P, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P]
+lib.aria_qlinear_w16a16.restype = _I
 
 
 class LinearProblem(ctypes.Structure):
@@ -102,15 +104,16 @@ def qpack_bytes(bits: int, group: int, K: int, N: int):
 
 def qpack(bits: int, w, q=None, s=None, stream=None):
     """Pack fp16 W [K][N]: bits 8 -> (Wq int8 [N][K], s fp16 [N]);
-    bits 4 -> (Wq4 uint8 [N][K/2], s fp16 [N][K/32])."""
+    bits 4 -> (Wq4 uint8 [N][K/2], s fp16 [N][K/32]); bits 16 -> (Wt fp16 [N][K], None)."""
     torch = _torch()
     _dt(w, torch.float16, "w")
     K, N = w.shape
-    group = 0 if bits == 8 else 32
+    group = 32 if bits == 4 else 0
     if q is None:
-        q = torch.empty((N, K) if bits == 8 else (N, K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
-                        device=w.device)
-    if s is None:
+        shape = (N, K // 2) if bits == 4 else (N, K)
+        dtype = {8: torch.int8, 4: torch.uint8, 16: torch.float16}[bits]
+        q = torch.empty(shape, dtype=dtype, device=w.device)
+    if s is None and bits != 16:
         s = torch.empty((N,) if bits == 8 else (N, K // group), dtype=torch.float16, device=w.device)
     _check(lib.aria_qpack(bits, group, _addr(w), K, N, _addr(q), _addr(s), _stream(stream)), "qpack")
     return q, s
@@ -192,6 +195,21 @@ def qlinear_w4a16(x, wq4, sg, y=None, ws=None, bias=None, gelu=False, residual=N
     e = _epi(bias, gelu, residual, steer_dir, steer_alpha, None)
     _check(lib.aria_qlinear_w4a16(_addr(x), M, K, N, _addr(wq4), _addr(sg), group, ctypes.byref(e), _addr(y),
                                   _addr(ws), nb, _stream(stream)), "qlinear_w4a16")
+    return y
+
+
+def qlinear_w16a16(x, wt, y=None, ws=None, bias=None, gelu=False, residual=None, steer_dir=None,
+                   steer_alpha=None, stream=None):
+    """The fp16 rung: Y = epilogue(X Wt^T) with Wt fp16 [N][K] from qpack(16, W)."""
+    torch = _torch()
+    _dt(x, torch.float16, "x"), _dt(wt, torch.float16, "wt")
+    M, K = x.shape
+    N = wt.shape[0]
+    y = _out(x, N, y)
+    ws, nb = _ws(ARIA_W16A16, M, K, N, ws, x.device)
+    e = _epi(bias, gelu, residual, steer_dir, steer_alpha, None)
+    _check(lib.aria_qlinear_w16a16(_addr(x), M, K, N, _addr(wt), ctypes.byref(e), _addr(y), _addr(ws), nb,
+                                   _stream(stream)), "qlinear_w16a16")
     return y
 
 

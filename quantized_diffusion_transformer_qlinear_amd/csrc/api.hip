@@ -92,6 +92,12 @@ int aria_qpack_bytes(int bits, int group, int64_t K, int64_t N, size_t* q_bytes,
         *s_bytes = (size_t)N * (size_t)(K / 32) * 2;
         return ARIA_OK;
     }
+    if (bits == 16 && group == 0) {
+        if (K * N >= ((int64_t)1 << 30)) return ARIA_E_SHAPE;   // 2 K N bytes, 32-bit offsets
+        *q_bytes = (size_t)(K * N) * 2;
+        *s_bytes = 0;
+        return ARIA_OK;
+    }
     return ARIA_E_UNSUPPORTED;
 }
 
@@ -100,12 +106,13 @@ int aria_qpack(int bits, int group, const void* w, int64_t K, int64_t N, void* q
     size_t qb, sb;
     const int rc = aria_qpack_bytes(bits, group, K, N, &qb, &sb);
     if (rc != ARIA_OK) return rc;
-    if (!w || !q || !s) return ARIA_E_NULL;
+    if (!w || !q || (!s && bits != 16)) return ARIA_E_NULL;
     if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return ARIA_E_ALIGN;
-    if (overlap(w, (size_t)(K * N) * 2, q, qb) || overlap(w, (size_t)(K * N) * 2, s, sb)) return ARIA_E_ALIAS;
+    if (overlap(w, (size_t)(K * N) * 2, q, qb) || (sb && overlap(w, (size_t)(K * N) * 2, s, sb))) return ARIA_E_ALIAS;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const half_t* wh = static_cast<const half_t*>(w);
+    if (bits == 16) return hip_status(launch_pack16(wh, K, N, static_cast<half_t*>(q), st));
     if (bits == 8) return hip_status(launch_qpack8(wh, K, N, static_cast<int8_t*>(q), static_cast<half_t*>(s), st));
     return hip_status(launch_qpack4(wh, K, N, static_cast<uint8_t*>(q), static_cast<half_t*>(s), st));
 }
@@ -126,6 +133,7 @@ size_t aria_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, int64_t N) {
         case ARIA_W8A8: return w8a8_ws(M, K);
         case ARIA_W8A16: return wxa16_workspace_bytes(8, M, K, N);
         case ARIA_W4A16: return wxa16_workspace_bytes(4, M, K, N);
+        case ARIA_W16A16: return wxa16_workspace_bytes(16, M, K, N);
         default: return 0;
     }
 }
@@ -154,11 +162,13 @@ static int wxa16(int bits, const void* x, int64_t M, int64_t K, int64_t N, const
                  const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
     int rc = check_shape(M, K, N);
     if (rc != ARIA_OK) return rc;
-    if (!x || !wq || !s || !y) return ARIA_E_NULL;
+    if (bits == 16 && K * N >= ((int64_t)1 << 30)) return ARIA_E_SHAPE;   // fp16 weights: 2 K N bytes
+    if (!x || !wq || (!s && bits != 16) || !y) return ARIA_E_NULL;
     if (!aligned16(x) || !aligned16(wq) || !aligned16(s) || !aligned16(y) || !aligned16(ws)) return ARIA_E_ALIGN;
     if (overlap(x, (size_t)(M * K) * 2, y, (size_t)(M * N) * 2)) return ARIA_E_ALIAS;
     Epi e;
-    if ((rc = make_epi(epi, bits == 8 ? ARIA_W8A16 : ARIA_W4A16, M, N, y, &e)) != ARIA_OK) return rc;
+    const int mode = bits == 8 ? ARIA_W8A16 : bits == 4 ? ARIA_W4A16 : ARIA_W16A16;
+    if ((rc = make_epi(epi, mode, M, N, y, &e)) != ARIA_OK) return rc;
     const size_t need = wxa16_workspace_bytes(bits, M, K, N);
     if (need && (!ws || ws_bytes < need)) return ARIA_E_WORKSPACE;
     (void)hipGetLastError();
@@ -236,6 +246,11 @@ int aria_qlinear_grouped(int bits, int group, const aria_linear_problem* problem
         if (rc != ARIA_OK) return rc;
     }
     return ARIA_OK;
+}
+
+int aria_qlinear_w16a16(const void* x, int64_t M, int64_t K, int64_t N, const void* wt, const aria_epilogue* epi,
+                        void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
+    return wxa16(16, x, M, K, N, wt, nullptr, epi, y, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

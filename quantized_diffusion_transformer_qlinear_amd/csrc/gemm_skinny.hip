@@ -4,6 +4,7 @@
 // put the 1.2 B model on an 8 GB device).
 //   W8A16: y = epilogue(s_w[n] * sum_k x[m][k] * q[n][k])
 //   W4A16: y = epilogue(sum_k x[m][k] * fp16(q4[n][k] * s_g[n][k/32]))
+//   W16A16 (the unquantized fp16 rung): y = epilogue(sum_k x[m][k] * wt[n][k])
 // M > 64 runs the tiled kernel (gemm_tiled.hip).
 //
 // Design (gfx950): a workgroup of 4 waves owns 16*CG output channels; each
@@ -32,7 +33,7 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // same order, so they produce bit-identical sums.
 template <int BITS, int MT, int CG, int NS>
 struct SkinnyRegs {
-    static constexpr int KPL = BITS == 8 ? 16 : 32;  // k per lane per 16-byte weight load
+    static constexpr int KPL = BITS == 8 ? 16 : BITS == 4 ? 32 : 8;  // k per lane per 16-byte weight load
     static constexpr int NQ = KPL / 8;               // 16x16x32 MFMAs fed by one load
     static constexpr int KPW = 4 * KPL;              // k per wave step (4 lane groups)
     static constexpr int KCH = 4 * NS * KPW;         // k per chunk
@@ -48,7 +49,7 @@ template <int BITS, int MT, int CG, int NS, bool SCALES = true>
 __device__ __forceinline__ void skinny_load(SkinnyRegs<BITS, MT, CG, NS>& R, rsrc_t rx, rsrc_t rw, rsrc_t rs,
                                             int M, int N, int K, int n0, int kc, int wave, int lane) {
     using RG = SkinnyRegs<BITS, MT, CG, NS>;
-    const uint32_t rowbytes = BITS == 8 ? (uint32_t)K : (uint32_t)K / 2;
+    const uint32_t rowbytes = BITS == 8 ? (uint32_t)K : BITS == 4 ? (uint32_t)K / 2 : (uint32_t)K * 2;
     const int G = K / 32;
     const int gsel = lane / 16;  // which k-run of a step this lane reads
 #pragma unroll
@@ -60,7 +61,7 @@ __device__ __forceinline__ void skinny_load(SkinnyRegs<BITS, MT, CG, NS>& R, rsr
         for (int g = 0; g < CG; g++) {
             const int col = n0 + 16 * g + lane % 16;
             const bool ok = in && col < N;
-            R.w[j][g] = buf_load16(rw, ok ? (uint32_t)col * rowbytes + (uint32_t)(BITS == 8 ? kb : kb / 2) : OOB);
+            R.w[j][g] = buf_load16(rw, ok ? (uint32_t)col * rowbytes + (uint32_t)(BITS == 8 ? kb : BITS == 4 ? kb / 2 : 2 * kb) : OOB);
             if (BITS == 4 && SCALES)
                 R.sc[j][g] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? ((uint32_t)col * G + kb / 32) * 2 : OOB), 0, 0);
         }
@@ -85,8 +86,10 @@ __device__ __forceinline__ void skinny_compute(const SkinnyRegs<BITS, MT, CG, NS
             v4i d[RG::NQ];
             if constexpr (BITS == 8) {
                 dec8(R.w[j][g], d[0], d[1]);
-            } else {
+            } else if constexpr (BITS == 4) {
                 dec4_bits(R.w[j][g], R.sc[j][g], d);
+            } else {
+                d[0] = R.w[j][g];   // fp16 weights: the load is the operand
             }
             // MFMA q of this run: the lane's 8 k are kb + 8q .. kb + 8q + 7 for its row and column
 #pragma unroll
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const half_t* __restri
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = threadIdx.x % WAVE;
     const int n0 = xcd_remap(blockIdx.x, gridDim.x) * 16 * CG;
     const rsrc_t rx = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2);
-    const rsrc_t rw = make_rsrc(Bq, (uint32_t)N * (BITS == 8 ? (uint32_t)K : (uint32_t)K / 2));
+    const rsrc_t rw = make_rsrc(Bq, (uint32_t)N * (BITS == 8 ? (uint32_t)K : BITS == 4 ? (uint32_t)K / 2 : (uint32_t)K * 2));
     const rsrc_t rs = make_rsrc(S, BITS == 4 ? (uint32_t)N * (uint32_t)(K / 32) * 2 : 0u);
     v4f acc[MT][CG];
 #pragma unroll
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_grouped_kernel(SkinnyGroup g)
     const int n0 = (b - P.first) * 16 * CG;
     const int G = P.K / 32;
     const rsrc_t rx = make_rsrc(P.x, (uint32_t)P.M * (uint32_t)P.K * 2);
-    const rsrc_t rw = make_rsrc(P.w, (uint32_t)P.N * (BITS == 8 ? (uint32_t)P.K : (uint32_t)P.K / 2));
+    const rsrc_t rw = make_rsrc(P.w, (uint32_t)P.N * (BITS == 8 ? (uint32_t)P.K : BITS == 4 ? (uint32_t)P.K / 2 : (uint32_t)P.K * 2));
     const rsrc_t rs = make_rsrc(P.s, BITS == 4 ? (uint32_t)P.N * (uint32_t)G * 2 : 0u);
     v4f acc[MT][CG];
 #pragma unroll
@@ -237,9 +240,10 @@ size_t wxa16_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
 
 namespace {
 
-// K-chunk of 1536 at both widths: NS = 3 steps of 128 k (4-bit) or 6 of 64 k (8-bit).
+// K-chunk of 1536 at every width: NS = 3 steps of 128 k (4-bit), 6 of 64 k
+// (8-bit) or 12 of 32 k (fp16).
 template <int BITS>
-constexpr int kNS = BITS == 8 ? 6 : 3;
+constexpr int kNS = BITS == 8 ? 6 : BITS == 4 ? 3 : 12;
 
 template <int BITS, int MT>
 hipError_t launch_skinny_mt(const half_t* x, const uint8_t* wq, const half_t* s, half_t* y, int M, int N, int K,
@@ -289,9 +293,12 @@ hipError_t launch_skinny_grouped(int bits, SkinnyGroup& g, hipStream_t st) {
 hipError_t launch_gemm_wxa16(int bits, const half_t* x, const void* wq, const half_t* s, half_t* y, int M,
                              int N, int K, const Epi& epi, void*, size_t, hipStream_t st) {
     const uint8_t* w = static_cast<const uint8_t*>(wq);
-    if (M <= 64)
-        return bits == 8 ? launch_skinny<8>(x, w, s, y, M, N, K, epi, st) : launch_skinny<4>(x, w, s, y, M, N, K, epi, st);
-    return launch_gemm_tiled(bits == 8 ? 1 : 2, x, wq, s, nullptr, y, M, N, K, epi, st);
+    if (M <= 64) {
+        if (bits == 8) return launch_skinny<8>(x, w, s, y, M, N, K, epi, st);
+        if (bits == 4) return launch_skinny<4>(x, w, s, y, M, N, K, epi, st);
+        return launch_skinny<16>(x, w, s, y, M, N, K, epi, st);
+    }
+    return launch_gemm_tiled(bits == 8 ? 1 : bits == 4 ? 2 : 3, x, wq, s, nullptr, y, M, N, K, epi, st);
 }
 
 }  // namespace aria

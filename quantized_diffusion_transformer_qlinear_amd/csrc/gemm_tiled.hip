@@ -1,11 +1,13 @@
-// a3+a4+a5 — the tiled quantized GEMM for M > 64, all three modes, with the
-// fused epilogue.
+// a3+a4+a5 — the tiled quantized GEMM for M > 64, all modes, with the fused
+// epilogue.
 //
 // What is computed (aria project page, "What aria is" / "Results": weights
-// stored at 8 or 4 bits; W8A8 runs 8-bit arithmetic on integer matrix units):
+// stored at 8 or 4 bits; W8A8 runs 8-bit arithmetic on integer matrix units;
+// fp16 is the unquantized row the modes are compared with):
 //   W8A8 : acc = sum_k Xq[m][k] * Wq[n][k] (exact int32);  y = acc * s_a[m] * s_w[n]
 //   W8A16: acc = sum_k X[m][k] * Wq[n][k]  (fp32; int8 -> fp16 is exact);  y = acc * s_w[n]
 //   W4A16: acc = sum_k X[m][k] * fp16(q4[n][k] * s_g[n][k/32])  (fp32);  y = acc
+//   W16A16: acc = sum_k X[m][k] * Wt[n][k]  (fp32);  y = acc
 // then y -> + bias -> GELU -> + residual -> + alpha d -> fp16.
 //
 // Design (gfx950): a workgroup of WM x WN waves owns a BM x BN output tile;
@@ -48,6 +50,11 @@ struct ModeT<2> {  // W4A16
     static constexpr int KSTEP = 64, AEB = 2, KPB = 32, BCH = 2;
     typedef v16f acc_t;
 };
+template <>
+struct ModeT<3> {  // W16A16 (fp16 weights, the unquantized rung)
+    static constexpr int KSTEP = 64, AEB = 2, KPB = 8, BCH = 8;
+    typedef v16f acc_t;
+};
 
 }  // namespace
 
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     const int wm = wave / WN, wn = wave % WN;
 
     const uint32_t abytes = (uint32_t)M * (uint32_t)K * T::AEB;
-    const uint32_t browb = MODE == 2 ? (uint32_t)K / 2 : (uint32_t)K;
+    const uint32_t browb = MODE == 2 ? (uint32_t)K / 2 : MODE == 3 ? (uint32_t)K * 2 : (uint32_t)K;
     const rsrc_t ra = make_rsrc(Aptr, abytes);
     const rsrc_t rb = make_rsrc(Bq, (uint32_t)N * browb);
     const int G = K / 32;
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
         const int c = (tid + i * NT) % NB, row = c / T::BCH, ch = c % T::BCH;
         const int k = kt * T::KSTEP + ch * T::KPB;
         const bool in = k < K && n0 + row < N;
-        const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : k);
+        const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : MODE == 3 ? 2 * k : k);
         RB[i] = buf_load16(rb, in ? off : OOB);
         if (MODE == 2) RS[i] = S[(int64_t)min(n0 + row, N - 1) * G + min(k, K - 32) / 32];
     };
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
         const int c = (tid + i * NT) % NB;
         const int row = c / T::BCH, ch = c % T::BCH;
         char* dst = &lds[buf][(BM + row) * ROWB + ch * (T::KPB * 2 / (MODE == 0 ? 2 : 1))];
-        if constexpr (MODE == 0) {
+        if constexpr (MODE == 0 || MODE == 3) {
             *reinterpret_cast<v4i*>(dst) = RB[i];
         } else if constexpr (MODE == 1) {
             v4i lo, hi;
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
             const int row = m0 + wm * WTM + i * 32 + rr, col = n0 + wn * WTN + cc * 8;
             const bool v = vec_ok && row < M && col + 8 <= N;
             const int64_t base = (int64_t)row * N + col;
-            sw8[t] = (MODE != 2 && v) ? *reinterpret_cast<const v8h*>(S + col) : zero8;
+            sw8[t] = ((MODE == 0 || MODE == 1) && v) ? *reinterpret_cast<const v8h*>(S + col) : zero8;
             sr[t] = (MODE == 0 && v) ? (float)sa[row] : 0.0f;
             r8[t] = (epi.residual && v) ? *reinterpret_cast<const v8h*>(epi.residual + base) : zero8;
         }
@@ -327,22 +334,22 @@ namespace {
 
 struct TileCfg {
     int bm, bn, wm, wn;
-    float eff[3];  // sustained throughput of one full wave of such tiles, per mode (relative units)
+    float eff[4];  // sustained throughput of one full wave of such tiles, per mode (relative units)
 };
 
 // Candidate macro tiles with their measured per-tile efficiency on MI355X
 // (throughput of a whole number of tile waves at M = 2048, K = 2048, by mode
-// W8A8 / W8A16 / W4A16).  The picker minimises
+// W8A8 / W8A16 / W4A16 / W16A16).  The picker minimises
 //   ceil(tiles / CUs) * BM * BN / eff
 // i.e. it trades CU fill (whole waves of tiles) against per-tile efficiency;
 // 8-wave workgroups put two waves on every SIMD so one can issue while the
 // other waits on LDS or memory.
 constexpr TileCfg kTiles[] = {
-    {256, 256, 4, 2, {1845.f, 1248.f, 1176.f}}, {256, 192, 4, 2, {1545.f, 970.f, 893.f}},
-    {256, 128, 4, 2, {1599.f, 1015.f, 856.f}},  {128, 256, 2, 4, {1605.f, 1008.f, 899.f}},
-    {128, 192, 2, 2, {1168.f, 744.f, 611.f}},   {128, 128, 2, 2, {1347.f, 795.f, 731.f}},
-    {64, 192, 2, 2, {1211.f, 706.f, 516.f}},    {128, 64, 2, 2, {1160.f, 672.f, 531.f}},
-    {64, 128, 2, 2, {1163.f, 619.f, 559.f}},    {64, 64, 2, 2, {1097.f, 570.f, 358.f}}};
+    {256, 256, 4, 2, {1845.f, 1248.f, 1176.f, 1248.f}}, {256, 192, 4, 2, {1545.f, 970.f, 893.f, 970.f}},
+    {256, 128, 4, 2, {1599.f, 1015.f, 856.f, 1015.f}},  {128, 256, 2, 4, {1605.f, 1008.f, 899.f, 1008.f}},
+    {128, 192, 2, 2, {1168.f, 744.f, 611.f, 744.f}},   {128, 128, 2, 2, {1347.f, 795.f, 731.f, 795.f}},
+    {64, 192, 2, 2, {1211.f, 706.f, 516.f, 706.f}},    {128, 64, 2, 2, {1160.f, 672.f, 531.f, 672.f}},
+    {64, 128, 2, 2, {1163.f, 619.f, 559.f, 619.f}},    {64, 64, 2, 2, {1097.f, 570.f, 358.f, 570.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -417,7 +424,8 @@ hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half
         hipError_t err;
         if (mode == 0) err = launch_mode<0>(t, ar, b, s, sar, yr, rows, N, K, e, st);
         else if (mode == 1) err = launch_mode<1>(t, ar, b, s, sar, yr, rows, N, K, e, st);
-        else err = launch_mode<2>(t, ar, b, s, sar, yr, rows, N, K, e, st);
+        else if (mode == 2) err = launch_mode<2>(t, ar, b, s, sar, yr, rows, N, K, e, st);
+        else err = launch_mode<3>(t, ar, b, s, sar, yr, rows, N, K, e, st);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

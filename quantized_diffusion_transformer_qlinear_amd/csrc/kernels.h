@@ -8,6 +8,7 @@ namespace aria {
 hipError_t launch_qpack8(const half_t* w, int64_t K, int64_t N, int8_t* q, half_t* s, hipStream_t st);
 hipError_t launch_qpack4(const half_t* w, int64_t K, int64_t N, uint8_t* q4, half_t* s, hipStream_t st);
 hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, half_t* sa, hipStream_t st);
+hipError_t launch_pack16(const half_t* w, int64_t K, int64_t N, half_t* wt, hipStream_t st);
 
 // Tiled contraction + epilogue for all modes (gemm_tiled.hip).  mode 0 = W8A8
 // (a = Xq int8 [M][K], sa = per-token scales), 1 = W8A16, 2 = W4A16 (a = X fp16).
@@ -15,7 +16,8 @@ hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half
                              int M, int N, int K, const Epi& epi, hipStream_t st);
 
 // Weight-only contraction + epilogue: A = X fp16 [M][K]; bits 8: B = Wq int8 [N][K] with
-// per-channel scales s [N]; bits 4: B = Wq4 [N][K/2] with group scales s [N][K/32].
+// per-channel scales s [N]; bits 4: B = Wq4 [N][K/2] with group scales s [N][K/32];
+// bits 16: B = Wt fp16 [N][K], no scales.
 // ws / ws_bytes: split-K partials for small M (may be null when not needed).
 hipError_t launch_gemm_wxa16(int bits, const half_t* x, const void* wq, const half_t* s, half_t* y,
                              int M, int N, int K, const Epi& epi, void* ws, size_t ws_bytes,

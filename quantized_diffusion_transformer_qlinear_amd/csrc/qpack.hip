@@ -119,6 +119,29 @@ __global__ __launch_bounds__(256) void qpack4_kernel(const half_t* __restrict__ 
     }
 }
 
+// The fp16 rung keeps fp16 weights in the same K-contiguous row layout as the
+// packed ones: Wt[n][k] = W[k][n], a transpose through a 64x64 LDS tile
+// (coalesced 128-byte rows on both sides).
+__global__ __launch_bounds__(256) void pack16_kernel(const half_t* __restrict__ w, int K, int N, half_t* __restrict__ wt) {
+    __shared__ half_t t[64][65];
+    const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64, c = threadIdx.x % 64;
+    for (int r = threadIdx.x / 64; r < 64; r += 4) {
+        const int k = k0 + r, n = n0 + c;
+        t[r][c] = (k < K && n < N) ? w[(int64_t)k * N + n] : (half_t)0.0f;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x / 64; r < 64; r += 4) {
+        const int n = n0 + r, k = k0 + c;
+        if (n < N && k < K) wt[(int64_t)n * K + k] = t[c][r];
+    }
+}
+
+hipError_t launch_pack16(const half_t* w, int64_t K, int64_t N, half_t* wt, hipStream_t st) {
+    dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64));
+    hipLaunchKernelGGL(pack16_kernel, grid, dim3(256), 0, st, w, (int)K, (int)N, wt);
+    return hipGetLastError();
+}
+
 hipError_t launch_qpack8(const half_t* w, int64_t K, int64_t N, int8_t* q, half_t* s, hipStream_t st) {
     dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N));
     hipLaunchKernelGGL(qpack8_kernel, grid, dim3(256), 0, st, w, K, N, q, s);

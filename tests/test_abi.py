@@ -29,7 +29,7 @@ def q():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (aria_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -48,7 +48,8 @@ def test_status_strings(q):
 def test_qpack_bytes(q):
     assert q.qpack_bytes(8, 0, 1536, 6144) == (1536 * 6144, 2 * 6144)
     assert q.qpack_bytes(4, 32, 1536, 6144) == (1536 * 6144 // 2, 2 * 6144 * 48)
-    for bits, group in ((8, 32), (4, 0), (4, 64), (2, 32)):
+    assert q.qpack_bytes(16, 0, 1536, 6144) == (2 * 1536 * 6144, 0)
+    for bits, group in ((8, 32), (4, 0), (4, 64), (2, 32), (16, 32)):
         with pytest.raises(q.AriaError) as e:
             q.qpack_bytes(bits, group, 64, 64)
         assert e.value.code == -4
@@ -104,6 +105,14 @@ def test_validation_codes(q):
     assert L.aria_qpack(8, 0, X, 64, 64, X + 64, S, None) == -7
     assert L.aria_quant_act(X, 64, 33, W, S, None) == -2
     assert L.aria_quant_act(X, 64, 64, None, S, None) == -1
+    # the fp16 rung
+    assert L.aria_qlinear_w16a16(X, 64, 256, 256, None, None, Y, None, 0, None) == -1
+    assert L.aria_qlinear_w16a16(X, 64, 48, 256, W, None, Y, None, 0, None) == -2
+    assert L.aria_qlinear_w16a16(X, 64, 16384, 65536, W, None, Y, None, 0, None) == -2   # 2 K N >= 2^31
+    assert L.aria_qlinear_w16a16(X + 4, 64, 256, 256, W, None, Y, None, 0, None) == -3
+    assert L.aria_qlinear_w16a16(X, 64, 256, 256, W, ctypes.byref(ep), Y, None, 0, None) == -4   # acc_out
+    assert L.aria_qpack(16, 32, X, 64, 64, W, None, None) == -4
+    assert L.aria_qpack(16, 0, None, 64, 64, W, None, None) == -1
     assert L.aria_qlinear_workspace_bytes(9, 64, 64, 64) == 0
     assert L.aria_qlinear_workspace_bytes(0, 64, 40, 64) == 0
 
