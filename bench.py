@@ -204,6 +204,43 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
     return res
 
 
+def precision_ladder(q, torch, dev, lin2, x_small, reps=20):
+    """The pages' precision ladder (fp16 / q8 / W8A8 / q4) restated for one
+    1536 -> 6144 layer (bias + GELU) at M = 2048 and at M = 16: microseconds
+    per call, eager launches timed with events (weights resident)."""
+    K, N = lin2.w.shape
+    wd = torch.from_numpy(lin2.w).to(dev)
+    packs = {16: q.qpack(16, wd), 8: q.qpack(8, wd), 4: q.qpack(4, wd)}
+    del wd
+    b = torch.from_numpy(lin2.bias).to(dev)
+    res = {}
+    for M, xs in ((2048, lin2.x), (16, x_small[:16])):
+        x = torch.from_numpy(xs[:M].copy()).to(dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = torch.empty(max(q.workspace_bytes(q.ARIA_W8A8, M, K, N), 1), dtype=torch.uint8, device=dev)
+        calls = {
+            "fp16 (W16A16)": lambda: q.qlinear_w16a16(x, packs[16][0], y=y, bias=b, gelu=True),
+            "q8 (W8A16)": lambda: q.qlinear_w8a16(x, *packs[8], y=y, bias=b, gelu=True),
+            "W8A8": lambda: q.qlinear_w8a8(x, *packs[8], y=y, ws=ws, bias=b, gelu=True),
+            "q4 (W4A16)": lambda: q.qlinear_w4a16(x, *packs[4], y=y, bias=b, gelu=True),
+        }
+        row = {}
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(e) / reps * 1e3
+            row[name] = {"us": round(us, 2), "tops": round(2.0 * M * K * N / us / 1e6, 1)}
+        res[f"M={M}"] = row
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,6 +415,7 @@ def main():
         out["copy_calibration"] = {"bytes": 2 * (256 << 20), "us": round(copy_us, 2),
                                    "GB/s": round(2 * (256 << 20) / copy_us / 1e3, 1)}
     out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
+    out["precision_ladder_1536x6144"] = precision_ladder(q, torch, dev, lin2, x3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
     print(json.dumps(out), flush=True)

@@ -345,11 +345,11 @@ struct TileCfg {
 // 8-wave workgroups put two waves on every SIMD so one can issue while the
 // other waits on LDS or memory.
 constexpr TileCfg kTiles[] = {
-    {256, 256, 4, 2, {1845.f, 1248.f, 1176.f, 1248.f}}, {256, 192, 4, 2, {1545.f, 970.f, 893.f, 970.f}},
-    {256, 128, 4, 2, {1599.f, 1015.f, 856.f, 1015.f}},  {128, 256, 2, 4, {1605.f, 1008.f, 899.f, 1008.f}},
-    {128, 192, 2, 2, {1168.f, 744.f, 611.f, 744.f}},   {128, 128, 2, 2, {1347.f, 795.f, 731.f, 795.f}},
-    {64, 192, 2, 2, {1211.f, 706.f, 516.f, 706.f}},    {128, 64, 2, 2, {1160.f, 672.f, 531.f, 672.f}},
-    {64, 128, 2, 2, {1163.f, 619.f, 559.f, 619.f}},    {64, 64, 2, 2, {1097.f, 570.f, 358.f, 570.f}}};
+    {256, 256, 4, 2, {1845.f, 1248.f, 1176.f, 1310.f}}, {256, 192, 4, 2, {1545.f, 970.f, 893.f, 1048.f}},
+    {256, 128, 4, 2, {1599.f, 1015.f, 856.f, 1066.f}},  {128, 256, 2, 4, {1605.f, 1008.f, 899.f, 1048.f}},
+    {128, 192, 2, 2, {1168.f, 744.f, 611.f, 818.f}},   {128, 128, 2, 2, {1347.f, 795.f, 731.f, 906.f}},
+    {64, 192, 2, 2, {1211.f, 706.f, 516.f, 741.f}},    {128, 64, 2, 2, {1160.f, 672.f, 531.f, 699.f}},
+    {64, 128, 2, 2, {1163.f, 619.f, 559.f, 656.f}},    {64, 64, 2, 2, {1097.f, 570.f, 358.f, 570.f}}};
 
 int num_cus() {
     static int cus = 0;
