@@ -19,7 +19,7 @@ eager pass times every call with events for the per-call breakdown and the
 dominant kernel's roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--eager] [--copy-calibration]
+                       [--eager] [--no-extras] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -248,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the small-M streaming and precision-ladder measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -414,8 +416,9 @@ def main():
     if copy_us is not None:
         out["copy_calibration"] = {"bytes": 2 * (256 << 20), "us": round(copy_us, 2),
                                    "GB/s": round(2 * (256 << 20) / copy_us / 1e3, 1)}
-    out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
-    out["precision_ladder_1536x6144"] = precision_ladder(q, torch, dev, lin2, x3)
+    if not args.no_extras:
+        out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
+        out["precision_ladder_1536x6144"] = precision_ladder(q, torch, dev, lin2, x3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
     print(json.dumps(out), flush=True)
