@@ -81,6 +81,8 @@ def _load():
             "or_pack16": [P, I64, I64, P],
             "or_ref_w16a16": [P, P, I64, I64, I64, P],
             "or_scale_w8a8": [P, P, P, I64, I64, P],
+            "or_layernorm": [P, P, P, ctypes.c_double, I64, I64, P],
+            "or_attention": [P, I64, I64, I64, I64, P],
             "or_epilogue": [P, I64, I64, P, ctypes.c_int, P, P, ctypes.c_float],
         }
         for name, args in sigs.items():
@@ -302,6 +304,47 @@ def qlinear_w16a16(x, wt, **epi) -> np.ndarray:
 
 def qlinear_w4a16(x, q4, s4, group=32, **epi) -> np.ndarray:
     return epilogue(ref_w4a16(x, q4, s4, group), **epi)
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-5) -> np.ndarray:
+    """LayerNorm over each row of x fp16 [M][W] with fp16 gamma, beta [W] (fp64 out)."""
+    x = _bits(x)
+    gamma = _bits(gamma)
+    beta = _bits(beta)
+    M, W = x.shape
+    assert gamma.shape == (W,) and beta.shape == (W,)
+    y = np.empty((M, W), np.float64)
+    _check(_load().or_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), float(eps), M, W, _ptr(y)), "layernorm")
+    return y
+
+
+def attention(qkv, heads: int, seq: int) -> np.ndarray:
+    """Multi-head softmax self-attention over [Q | K | V] = qkv fp16 [M][3W]
+    within each sequence of `seq` rows (fp64 out [M][W])."""
+    qkv = _bits(qkv)
+    M, W3 = qkv.shape
+    W = W3 // 3
+    out = np.empty((M, W), np.float64)
+    _check(_load().or_attention(_ptr(qkv), M, W, int(heads), int(seq), _ptr(out)), "attention")
+    return out
+
+
+def dit_block_full_w8a8(h, packed, ln1, ln2, heads: int, seq: int, d=None, alpha=0.0, eps: float = 1e-5):
+    """The W8A8 DiT block with its attention core and norms, rounding to fp16
+    at every stage boundary as the device stores it:
+      n1 = LN1(h);  qkv = n1.Wqkv;  a = attention(qkv);  h1 = h + a.Wo;
+      n2 = LN2(h1);  u = gelu(n2.Wup);  out = h1 + u.Wdown + alpha*d.
+    ``ln1`` / ``ln2`` are (gamma, beta) pairs.  Returns the fp16 stage outputs
+    and the fp64 value of the last stage."""
+    h = np.asarray(h, np.float16)
+    n1 = f64_to_f16(layernorm(h, *ln1, eps))
+    qkv = f64_to_f16(qlinear_w8a8(n1, *packed["qkv"])["y"])
+    a = f64_to_f16(attention(qkv, heads, seq))
+    h1 = f64_to_f16(qlinear_w8a8(a, *packed["o"], residual=h)["y"])
+    n2 = f64_to_f16(layernorm(h1, *ln2, eps))
+    u = f64_to_f16(qlinear_w8a8(n2, *packed["up"], gelu=True)["y"])
+    out64 = qlinear_w8a8(u, *packed["down"], residual=h1, d=d, alpha=alpha)["y"]
+    return {"n1": n1, "qkv": qkv, "a": a, "h1": h1, "n2": n2, "u": u, "out": f64_to_f16(out64), "out64": out64}
 
 
 def dit_block_w8a8(h, packed, d=None, alpha=0.0):

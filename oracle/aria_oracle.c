@@ -337,3 +337,78 @@ int or_epilogue(double* y, int64_t M, int64_t N, const uint16_t* bias, int gelu,
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* The steps on either side of the linears in a DiT block ([P5] Fig. 1 "DiT  */
+/* blocks"; [P4] "What aria is": the denoiser is a transformer over latent   */
+/* tokens).  The pages name the blocks but not their internals; the plain    */
+/* readings (design notes R21-R23): a pre-norm LayerNorm per token over the  */
+/* width, and multi-head softmax self-attention with 64-dimensional heads,   */
+/* no mask and no position terms, within each sequence of S tokens.          */
+/* ------------------------------------------------------------------------- */
+
+/* LayerNorm over each row (Ba, Kiros, Hinton, "Layer Normalization"):
+ *   mu = mean_k x[m][k];  var = mean_k (x[m][k] - mu)^2   (population)
+ *   y[m][k] = (x[m][k] - mu) / sqrt(var + eps) * gamma[k] + beta[k]   (fp64). */
+int or_layernorm(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, double eps,
+                 int64_t M, int64_t W, double* y)
+{
+    if (!x || !gamma || !beta || !y || M <= 0 || W <= 0 || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        double mu = 0.0, var = 0.0;
+        for (int64_t k = 0; k < W; k++) mu += or_f16_to_f64(x[m * W + k]);
+        mu /= (double)W;
+        for (int64_t k = 0; k < W; k++) {
+            double c = or_f16_to_f64(x[m * W + k]) - mu;
+            var += c * c;
+        }
+        var /= (double)W;
+        double inv = 1.0 / sqrt(var + eps);
+        for (int64_t k = 0; k < W; k++)
+            y[m * W + k] = (or_f16_to_f64(x[m * W + k]) - mu) * inv * or_f16_to_f64(gamma[k]) +
+                           or_f16_to_f64(beta[k]);
+    }
+    return 0;
+}
+
+/* Multi-head self-attention (Vaswani et al., "Attention Is All You Need"):
+ * qkv fp16 [M][3W] holds [Q | K | V] column blocks, head h of each at columns
+ * h*D .. h*D + D - 1 (D = W / H).  The M rows are M / S independent sequences
+ * of S tokens.  For sequence b, head h, query i:
+ *   s_j = (q_i . k_j) / sqrt(D),  p_j = exp(s_j - max s) / sum exp(...),
+ *   out[i][h*D + e] = sum_j p_j v_j[e]                                  (fp64). */
+int or_attention(const uint16_t* qkv, int64_t M, int64_t W, int64_t H, int64_t S, double* out)
+{
+    if (!qkv || !out || M <= 0 || W <= 0 || H <= 0 || S <= 0 || W % H || M % S) return -1;
+    const int64_t D = W / H, ld = 3 * W;
+    const double scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t b = 0; b < M / S; b++)
+        for (int64_t h = 0; h < H; h++) {
+            double* sc = (double*)malloc((size_t)S * sizeof(double));
+            for (int64_t i = 0; i < S; i++) {
+                const int64_t qi = (b * S + i) * ld + h * D;
+                double mx = -INFINITY;
+                for (int64_t j = 0; j < S; j++) {
+                    const int64_t kj = (b * S + j) * ld + W + h * D;
+                    double t = 0.0;
+                    for (int64_t e = 0; e < D; e++) t += or_f16_to_f64(qkv[qi + e]) * or_f16_to_f64(qkv[kj + e]);
+                    sc[j] = t * scale;
+                    if (sc[j] > mx) mx = sc[j];
+                }
+                double sum = 0.0;
+                for (int64_t j = 0; j < S; j++) {
+                    sc[j] = exp(sc[j] - mx);
+                    sum += sc[j];
+                }
+                for (int64_t e = 0; e < D; e++) {
+                    double o = 0.0;
+                    for (int64_t j = 0; j < S; j++) o += sc[j] * or_f16_to_f64(qkv[(b * S + j) * ld + 2 * W + h * D + e]);
+                    out[(b * S + i) * W + h * D + e] = o / sum;
+                }
+            }
+            free(sc);
+        }
+    return 0;
+}

@@ -18,7 +18,7 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "aria_oracle.c")
 PIN_FILES = ["tests/test_oracle_codec.py", "tests/test_oracle_quant.py", "tests/test_oracle_pack.py",
-             "tests/test_oracle_gemm.py", "tests/test_oracle_epilogue.py"]
+             "tests/test_oracle_gemm.py", "tests/test_oracle_epilogue.py", "tests/test_oracle_block.py"]
 
 MUTANTS = {
     "rne_ties_up": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
@@ -45,6 +45,14 @@ MUTANTS = {
     "steer_always": ("if (d && alpha != 0.0f)", "if (d)"),
     "pack16_not_transposed": ("wt[n * K + k] = w[k * N + n];", "wt[n * K + k] = w[n * K + k];"),
     "w16a16_row_stride": ("t += xr[k] * or_f16_to_f64(wt[n * K + k]);", "t += xr[k] * or_f16_to_f64(wt[k * N + n]);"),
+    "layernorm_no_eps": ("double inv = 1.0 / sqrt(var + eps);", "double inv = 1.0 / sqrt(var);"),
+    "layernorm_sample_variance": ("var /= (double)W;", "var /= (double)(W - 1);"),
+    "layernorm_beta_scaled": ("* or_f16_to_f64(gamma[k]) +\n                           or_f16_to_f64(beta[k]);",
+                              "* or_f16_to_f64(gamma[k]) * (1.0 +\n                           or_f16_to_f64(beta[k]));"),
+    "attention_no_scale": ("const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0;"),
+    "attention_across_sequences": ("const int64_t kj = (b * S + j) * ld + W + h * D;", "const int64_t kj = (((b + 1) % (M / S)) * S + j) * ld + W + h * D;"),
+    "attention_value_head": ("o += sc[j] * or_f16_to_f64(qkv[(b * S + j) * ld + 2 * W + h * D + e]);",
+                             "o += sc[j] * or_f16_to_f64(qkv[(b * S + j) * ld + 2 * W + e]);"),
 }
 
 
