@@ -241,6 +241,57 @@ def precision_ladder(q, torch, dev, lin2, x_small, reps=20):
     return res
 
 
+def full_block(q, torch, dev, si, blk, packed, reps=20):
+    """The W8A8 DiT block with its attention core and pre-norms (LN1, QKV,
+    attention over 2 x 1024 tokens with 24 heads of 64, out + residual, LN2,
+    MLP-up + GELU, MLP-down + residual + alpha*d) at M = 2048: graph-replayed
+    microseconds per block and an eager per-stage breakdown."""
+    from quantized_diffusion_transformer_qlinear_amd.chain import DitBlockFullW8A8
+    norms = si.dit_block_norms()
+    ln1 = tuple(torch.from_numpy(a).to(dev) for a in norms["ln1"])
+    ln2 = tuple(torch.from_numpy(a).to(dev) for a in norms["ln2"])
+    alpha = torch.tensor([blk["alpha"]], dtype=torch.float32, device=dev)
+    chain = DitBlockFullW8A8(packed, ln1, ln2, si.TOKENS, si.WIDTH, si.MLP, si.HEADS, si.SEQ,
+                             steer_dir=torch.from_numpy(blk["d"]).to(dev), steer_alpha=alpha)
+    h = torch.from_numpy(blk["h"]).to(dev)
+    names = ["ln1", "qkv", "attention", "out", "ln2", "up", "down"]
+    for _ in range(3):
+        chain.run(h)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        chain.run(h)
+        with torch.cuda.graph(g, stream=st):
+            chain.run(h)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    us_graph = a.elapsed_time(e) / reps * 1e3
+    per = {n: 0.0 for n in names}
+    for _ in range(reps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        evs[0].record()
+        for i, _n in enumerate(chain.stages(h)):
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            per[n] += evs[i].elapsed_time(evs[i + 1]) * 1e3 / reps
+    W, F, M = si.WIDTH, si.MLP, si.TOKENS
+    lin_ops = 2.0 * M * W * (3 * W + W + F) + 2.0 * M * F * W
+    attn_flops = 2 * 2.0 * M * si.SEQ * W          # QK^T and PV over each sequence
+    return {"us_per_block_graph": round(us_graph, 2),
+            "stages_us_eager": {n: round(v, 2) for n, v in per.items()},
+            "attention_tflops": round(attn_flops / per["attention"] / 1e6, 1),
+            "ops_per_block": {"linears": lin_ops, "attention": attn_flops},
+            "tops_incl_attention": round((lin_ops + attn_flops) / us_graph / 1e6, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,6 +470,7 @@ def main():
     if not args.no_extras:
         out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
         out["precision_ladder_1536x6144"] = precision_ladder(q, torch, dev, lin2, x3)
+        out["dit_block_full_m2048"] = full_block(q, torch, dev, si, blk, packed)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
     print(json.dumps(out), flush=True)

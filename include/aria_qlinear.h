@@ -155,6 +155,28 @@ int aria_qlinear_w16a16(const void* x_f16, int64_t M, int64_t K, int64_t N, cons
                         const aria_epilogue* epi, void* y_f16, void* ws, size_t ws_bytes,
                         aria_stream_t stream);
 
+/* The DiT block's steps on either side of its linears (docshare paper page,
+ * Fig. 1 "DiT blocks"; project page, "What aria is": the denoiser is a
+ * transformer over latent tokens).  The pages name the block, not its
+ * internals; these are the plain pre-norm transformer readings. */
+
+/* LayerNorm of every row of X fp16 [M][W] (population variance, in fp32):
+ * Y = (x - mean) / sqrt(var + eps) * gamma + beta, gamma / beta fp16 [W],
+ * Y fp16 [M][W].  8 <= W <= 16384, W % 8 == 0, 0 <= eps <= 1.  y may be x
+ * (in place) but must not partly overlap it. */
+int aria_layernorm(const void* x_f16, int64_t M, int64_t W, const void* gamma_f16, const void* beta_f16,
+                   float eps, void* y_f16, aria_stream_t stream);
+
+/* Multi-head softmax self-attention: qkv fp16 [M][3W] holds [Q | K | V]
+ * column blocks (the QKV linear's output), head h of each at columns
+ * h*64 .. h*64+63; the M rows are M / seq independent sequences of seq rows.
+ *   out[i][h*64 + e] = sum_j softmax_j(q_i . k_j / 8) v_j[e]
+ * with fp32 scores, softmax and accumulation, fp16 probabilities and output
+ * out fp16 [M][W].  W must be heads * 64 (ARIA_E_UNSUPPORTED otherwise);
+ * M % seq == 0; out must not overlap qkv. */
+int aria_attention(const void* qkv_f16, int64_t M, int64_t W, int64_t heads, int64_t seq, void* out_f16,
+                   aria_stream_t stream);
+
 /* One weight-only linear of a grouped call: Y = epilogue(X * dequant(Wq)) as in
  * aria_qlinear_w8a16 / aria_qlinear_w4a16.  epi is a host pointer or NULL
  * (acc_out must be NULL). */

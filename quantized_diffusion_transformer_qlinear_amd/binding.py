@@ -45,6 +45,12 @@ lib.aria_qlinear_w16a16.argtypes = [_P, _I64, _I64, _I64, _P, ctypes.POINTER(Epi
 lib.aria_qlinear_w16a16.restype = _I
 
 
+lib.aria_layernorm.argtypes = [_P, _I64, _I64, _P, _P, ctypes.c_float, _P, _P]
+lib.aria_layernorm.restype = _I
+lib.aria_attention.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P]
+lib.aria_attention.restype = _I
+
+
 class LinearProblem(ctypes.Structure):
     _fields_ = [("x_f16", _P), ("M", _I64), ("K", _I64), ("N", _I64), ("wq", _P), ("s_f16", _P),
                 ("epi", ctypes.POINTER(Epilogue)), ("y_f16", _P)]
@@ -236,3 +242,26 @@ def qlinear_grouped(bits: int, problems, stream=None):
     _check(lib.aria_qlinear_grouped(bits, 0 if bits == 8 else 32, arr, len(problems), _stream(stream)),
            "qlinear_grouped")
     return outs
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-5, y=None, stream=None):
+    """LayerNorm of every row of x fp16 [M][W] (y may be x)."""
+    torch = _torch()
+    _dt(x, torch.float16, "x"), _dt(gamma, torch.float16, "gamma"), _dt(beta, torch.float16, "beta")
+    M, W = x.shape
+    y = torch.empty_like(x) if y is None else y
+    _check(lib.aria_layernorm(_addr(x), M, W, _addr(gamma), _addr(beta), float(eps), _addr(y), _stream(stream)),
+           "layernorm")
+    return y
+
+
+def attention(qkv, heads: int, seq: int, out=None, stream=None):
+    """Multi-head self-attention over [Q | K | V] = qkv fp16 [M][3W] within
+    sequences of `seq` rows; returns out fp16 [M][W]."""
+    torch = _torch()
+    _dt(qkv, torch.float16, "qkv")
+    M, W3 = qkv.shape
+    W = W3 // 3
+    out = torch.empty((M, W), dtype=torch.float16, device=qkv.device) if out is None else out
+    _check(lib.aria_attention(_addr(qkv), M, W, int(heads), int(seq), _addr(out), _stream(stream)), "attention")
+    return out

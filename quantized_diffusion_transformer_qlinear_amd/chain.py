@@ -71,3 +71,54 @@ class DitBlockW8A8:
         for _ in self.stages(h, stream):
             pass
         return self.out
+
+
+class DitBlockFullW8A8:
+    """The W8A8 block with its attention core and pre-norms (docshare paper
+    page, Fig. 1 "DiT blocks"):
+      n1 = LN1(h);  qkv = n1.Wqkv;  a = attention(qkv);  h1 = h + a.Wo;
+      n2 = LN2(h1); u = gelu(n2.Wup); out = h1 + u.Wdown + alpha*d,
+    with `heads` 64-dimensional heads over sequences of `seq` tokens (the M
+    rows hold M / seq sequences, e.g. two guidance branches).  Every step runs
+    in the library's kernels; ``run(h)`` returns the block output."""
+
+    def __init__(self, packed: dict, ln1, ln2, M: int, width: int, mlp: int, heads: int, seq: int,
+                 steer_dir=None, steer_alpha=None, eps: float = 1e-5):
+        import torch
+        dev = packed["qkv"][0].device
+        self.packed, self.ln1, self.ln2, self.eps = packed, ln1, ln2, eps
+        self.M, self.width, self.mlp, self.heads, self.seq = M, width, mlp, heads, seq
+        self.steer_dir, self.steer_alpha = steer_dir, steer_alpha
+        f16 = torch.float16
+        self.n1 = torch.empty((M, width), dtype=f16, device=dev)
+        self.qkv = torch.empty((M, 3 * width), dtype=f16, device=dev)
+        self.a = torch.empty((M, width), dtype=f16, device=dev)
+        self.h1 = torch.empty((M, width), dtype=f16, device=dev)
+        self.n2 = torch.empty((M, width), dtype=f16, device=dev)
+        self.u = torch.empty((M, mlp), dtype=f16, device=dev)
+        self.out = torch.empty((M, width), dtype=f16, device=dev)
+        need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, 1) for k in (width, mlp))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def stages(self, h, stream=None):
+        p = self.packed
+        B.layernorm(h, *self.ln1, eps=self.eps, y=self.n1, stream=stream)
+        yield "ln1"
+        B.qlinear_w8a8(self.n1, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)
+        yield "qkv"
+        B.attention(self.qkv, self.heads, self.seq, out=self.a, stream=stream)
+        yield "attention"
+        B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)
+        yield "out"
+        B.layernorm(self.h1, *self.ln2, eps=self.eps, y=self.n2, stream=stream)
+        yield "ln2"
+        B.qlinear_w8a8(self.n2, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)
+        yield "up"
+        B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
+                       steer_dir=self.steer_dir, steer_alpha=self.steer_alpha, stream=stream)
+        yield "down"
+
+    def run(self, h, stream=None):
+        for _ in self.stages(h, stream):
+            pass
+        return self.out

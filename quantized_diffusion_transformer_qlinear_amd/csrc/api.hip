@@ -248,6 +248,32 @@ int aria_qlinear_grouped(int bits, int group, const aria_linear_problem* problem
     return ARIA_OK;
 }
 
+int aria_layernorm(const void* x, int64_t M, int64_t W, const void* gamma, const void* beta, float eps, void* y,
+                   aria_stream_t stream) {
+    if (M < 1 || M > kMaxDim || W < 8 || W > kMaxK || W % 8 != 0) return ARIA_E_SHAPE;
+    if (!(eps >= 0.0f) || eps > 1.0f) return ARIA_E_UNSUPPORTED;
+    if (!x || !gamma || !beta || !y) return ARIA_E_NULL;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || !aligned16(y)) return ARIA_E_ALIGN;
+    const size_t xb = (size_t)(M * W) * 2;
+    if (y != x && overlap(x, xb, y, xb)) return ARIA_E_ALIAS;   // in place is fine: a row is read before written
+    (void)hipGetLastError();
+    return hip_status(launch_layernorm(static_cast<const half_t*>(x), static_cast<const half_t*>(gamma),
+                                       static_cast<const half_t*>(beta), eps, M, W, static_cast<half_t*>(y),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int aria_attention(const void* qkv, int64_t M, int64_t W, int64_t heads, int64_t seq, void* out, aria_stream_t stream) {
+    if (M < 1 || M > kMaxDim || heads < 1 || seq < 1 || M % seq != 0) return ARIA_E_SHAPE;
+    if (W != heads * 64) return ARIA_E_UNSUPPORTED;                      // 64-dimensional heads only
+    if (seq * 3 * W * 2 >= ((int64_t)1 << 31) || heads > 65535 || M / seq > 65535) return ARIA_E_SHAPE;
+    if (!qkv || !out) return ARIA_E_NULL;
+    if (!aligned16(qkv) || !aligned16(out)) return ARIA_E_ALIGN;
+    if (overlap(qkv, (size_t)(M * 3 * W) * 2, out, (size_t)(M * W) * 2)) return ARIA_E_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(launch_attention(static_cast<const half_t*>(qkv), M, W, heads, seq, static_cast<half_t*>(out),
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int aria_qlinear_w16a16(const void* x, int64_t M, int64_t K, int64_t N, const void* wt, const aria_epilogue* epi,
                         void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
     return wxa16(16, x, M, K, N, wt, nullptr, epi, y, ws, ws_bytes, stream);

@@ -1,0 +1,177 @@
+// The DiT block's attention core between the QKV and out-projection linears
+// (docshare paper page, Fig. 1 "DiT blocks"; project page, "What aria is": the
+// denoiser is a transformer over latent tokens).  Multi-head softmax
+// self-attention over [Q | K | V] = qkv fp16 [M][3W], head h of each block at
+// columns h*64 .. h*64+63, within each sequence of S consecutive rows:
+//   out[i][h*64 + e] = sum_j softmax_j(q_i . k_j / 8) v_j[e]     (64-dim heads)
+//
+// Design (gfx950, flash-attention style, one pass over the keys): a workgroup
+// of 4 waves owns 128 queries of one (sequence, head); each wave keeps its 32
+// queries' Q fragments in registers and computes S^T = K Q^T, so that a lane
+// holds the scores of ONE query (column l % 32) for 32 keys: the running max
+// and sum of the online softmax need one cross-lane exchange per key block
+// instead of a reduction over 32 lanes.  P^T (fp16) is fed straight from the
+// score registers as the B operand of O^T += V^T P^T; the key order that the
+// score layout implies is matched by how V^T is read from LDS.  Key blocks of
+// 64 are double-buffered in LDS (K row-major with a 16-byte row pad, V stored
+// transposed), the next block's loads are in flight during the current
+// block's matrix work, one barrier per block.  Scores, the softmax and the
+// accumulators are fp32; P and the output are rounded to fp16.
+#include "common.h"
+#include "kernels.h"
+
+namespace aria {
+
+namespace {
+
+constexpr int HD = 64;        // head dimension
+constexpr int KB = 64;        // keys per block
+constexpr int QW = 4;         // waves per workgroup (32 queries each)
+constexpr int KROW = HD + 8;  // K rows in LDS, halves (16-byte pad)
+constexpr int VROW = KB + 8;  // V^T rows in LDS, halves
+
+__device__ __forceinline__ float wave_xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, WAVE)); }
+__device__ __forceinline__ float wave_xor32_sum(float v) { return v + __shfl_xor(v, 32, WAVE); }
+
+}  // namespace
+
+__global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __restrict__ qkv, int M, int W, int S,
+                                                              half_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) half_t Ks[2][KB][KROW];
+    __shared__ __attribute__((aligned(16))) half_t Vt[2][HD][VROW];
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE, hl = lane / 32;
+    const int h = blockIdx.y, seq = blockIdx.z;
+    const int q0 = blockIdx.x * (QW * 32) + wave * 32;  // this wave's first query (within the sequence)
+    const int ld = 3 * W;                               // qkv row stride, halves
+    const int64_t row0 = (int64_t)seq * S;              // first row of the sequence
+    const rsrc_t rq = make_rsrc(qkv + row0 * ld, (uint32_t)S * (uint32_t)ld * 2);
+
+    // Q^T fragments (B operand): lane = query q0 + lane % 32, d = 16 t + 8 hl .. +7
+    v8h qf[4];
+    {
+        const int q = q0 + lane % 32;
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            qf[t] = __builtin_bit_cast(v8h, buf_load16(rq, q < S ? ((uint32_t)q * ld + h * HD + 16 * t + 8 * hl) * 2 : OOB));
+    }
+
+    // cooperative K / V block loads: 512 chunks of 16 bytes each, 2 + 2 per thread
+    v4i rk[2], rv[2];
+    auto load_kv = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int c = tid + i * QW * WAVE, key = c / 8, piece = c % 8, j = kb + key;
+            const uint32_t base = (uint32_t)j * ld + h * HD + piece * 8;
+            rk[i] = buf_load16(rq, j < S ? (base + W) * 2 : OOB);
+            rv[i] = buf_load16(rq, j < S ? (base + 2 * W) * 2 : OOB);
+        }
+    };
+    auto store_kv = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int c = tid + i * QW * WAVE, key = c / 8, piece = c % 8;
+            *reinterpret_cast<v4i*>(&Ks[buf][key][piece * 8]) = rk[i];
+            const v8h v = __builtin_bit_cast(v8h, rv[i]);
+#pragma unroll
+            for (int e = 0; e < 8; e++) Vt[buf][piece * 8 + e][key] = v[e];
+        }
+    };
+
+    // scores in the log2 domain: s * (1/sqrt(64)) * log2(e)
+    const float sl2 = 0.125f * 1.4426950408889634f;
+    float m = -INFINITY, lsum = 0.0f;
+    v16f ot[2] = {v16f{}, v16f{}};
+    const int nkb = (S + KB - 1) / KB;
+    load_kv(0);
+    store_kv(0);
+    if (nkb > 1) load_kv(KB);
+    __syncthreads();
+    for (int b = 0; b < nkb; b++) {
+        const int cur = b & 1, kb = b * KB;
+        // S^T tiles: keys 32 jt + (row), queries (column = lane % 32)
+        v16f st[2] = {v16f{}, v16f{}};
+#pragma unroll
+        for (int jt = 0; jt < 2; jt++)
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const v8h kf = *reinterpret_cast<const v8h*>(&Ks[cur][32 * jt + lane % 32][16 * t + 8 * hl]);
+                st[jt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[t], st[jt], 0, 0, 0);
+            }
+        // online softmax for this lane's query over the block's 64 keys
+        float mb = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < 2; jt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int key = kb + 32 * jt + 8 * (r / 4) + 4 * hl + r % 4;
+                const float sv = st[jt][r];
+                const float s2 = key < S ? sv * sl2 : -INFINITY;
+                st[jt][r] = s2;
+                mb = fmaxf(mb, s2);
+            }
+        mb = wave_xor32_max(mb);
+        const float mn = fmaxf(m, mb);
+        const float corr = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block (m = -inf)
+        float ps = 0.0f;
+        v8h pf[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float p = __builtin_amdgcn_exp2f(st[u / 2][8 * (u % 2) + e] - mn);
+                ps += p;
+                pf[u][e] = (half_t)p;
+            }
+        lsum = lsum * corr + wave_xor32_sum(ps);
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < 2; dt++) ot[dt] *= corr;
+        // O^T += V^T P^T over the block's 4 k-steps of 16 keys; register e of
+        // P^T step u is key 16 u + 4 hl + 8 (e / 4) + e % 4
+#pragma unroll
+        for (int dt = 0; dt < 2; dt++)
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const half_t* vr = &Vt[cur][32 * dt + lane % 32][16 * u + 4 * hl];
+                const v2u lo = *reinterpret_cast<const v2u*>(vr);
+                const v2u hi = *reinterpret_cast<const v2u*>(vr + 8);
+                const v8h vf = __builtin_bit_cast(v8h, v4u{lo[0], lo[1], hi[0], hi[1]});
+                ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[u], ot[dt], 0, 0, 0);
+            }
+        // the next block: stored into the other buffer (free since the last
+        // barrier), the one after it requested
+        if (b + 1 < nkb) {
+            store_kv(cur ^ 1);
+            if (b + 2 < nkb) load_kv(kb + 2 * KB);
+        }
+        __syncthreads();
+    }
+
+    // out[query][h*64 + d] = O^T[d][query] / sum; register r of tile dt is
+    // d = 32 dt + 8 (r / 4) + 4 hl + r % 4: four consecutive d per 8-byte store
+    const int q = q0 + lane % 32;
+    if (q < S) {
+        const float inv = 1.0f / lsum;
+        half_t* orow = out + (row0 + q) * W + h * HD;
+#pragma unroll
+        for (int dt = 0; dt < 2; dt++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+
+                const float a0 = ot[dt][4 * g], a1 = ot[dt][4 * g + 1], a2 = ot[dt][4 * g + 2], a3 = ot[dt][4 * g + 3];
+                const v2h p0 = {(half_t)(a0 * inv), (half_t)(a1 * inv)};
+                const v2h p1 = {(half_t)(a2 * inv), (half_t)(a3 * inv)};
+                *reinterpret_cast<v2u*>(orow + 32 * dt + 8 * g + 4 * hl) =
+                    v2u{__builtin_bit_cast(u32, p0), __builtin_bit_cast(u32, p1)};
+            }
+    }
+}
+
+hipError_t launch_attention(const half_t* qkv, int64_t M, int64_t W, int64_t H, int64_t S, half_t* out,
+                            hipStream_t st) {
+    dim3 grid((unsigned)((S + QW * 32 - 1) / (QW * 32)), (unsigned)H, (unsigned)(M / S));
+    hipLaunchKernelGGL(attention_kernel, grid, dim3(QW * WAVE), 0, st, qkv, (int)M, (int)W, (int)S, out);
+    return hipGetLastError();
+}
+
+}  // namespace aria

@@ -10,6 +10,12 @@ hipError_t launch_qpack4(const half_t* w, int64_t K, int64_t N, uint8_t* q4, hal
 hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, half_t* sa, hipStream_t st);
 hipError_t launch_pack16(const half_t* w, int64_t K, int64_t N, half_t* wt, hipStream_t st);
 
+// The DiT block's steps around the linears (layernorm.hip, attention.hip).
+hipError_t launch_layernorm(const half_t* x, const half_t* gamma, const half_t* beta, float eps, int64_t M, int64_t W,
+                            half_t* y, hipStream_t st);
+hipError_t launch_attention(const half_t* qkv, int64_t M, int64_t W, int64_t H, int64_t S, half_t* out,
+                            hipStream_t st);
+
 // Tiled contraction + epilogue for all modes (gemm_tiled.hip).  mode 0 = W8A8
 // (a = Xq int8 [M][K], sa = per-token scales), 1 = W8A16, 2 = W4A16 (a = X fp16).
 hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half_t* s, const half_t* sa, half_t* y,

@@ -23,9 +23,12 @@ MLP = 6144
 TOKENS = 2048  # 2 classifier-free-guidance branches x 1024 latent tokens
 
 
-def normal_f16(shape, sigma: float, seed: int) -> np.ndarray:
+def normal_f16(shape, sigma: float, seed: int, offset: float = 0.0) -> np.ndarray:
     rng = np.random.default_rng(seed)
-    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)).astype(np.float16)
+    v = rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+    if offset:
+        v = v + np.float32(offset)
+    return v.astype(np.float16)
 
 
 def unit_direction(n: int, seed: int) -> np.ndarray:
@@ -78,6 +81,18 @@ def dit_block() -> dict:
         "down": normal_f16((MLP, WIDTH), 0.02, 405),
         "d": unit_direction(WIDTH, 406),
         "alpha": 0.3,
+    }
+
+
+HEADS = 24      # 64-dimensional attention heads at width 1536
+SEQ = 1024      # latent tokens per guidance branch
+
+
+def dit_block_norms() -> dict:
+    """LayerNorm parameters of the full block: gamma ~ 1 + N(0, 0.1), beta ~ N(0, 0.1)."""
+    return {
+        "ln1": (normal_f16((WIDTH,), 0.1, 407, offset=1.0), normal_f16((WIDTH,), 0.1, 408)),
+        "ln2": (normal_f16((WIDTH,), 0.1, 409, offset=1.0), normal_f16((WIDTH,), 0.1, 410)),
     }
 
 

@@ -29,7 +29,7 @@ def q():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (aria_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -113,6 +113,18 @@ def test_validation_codes(q):
     assert L.aria_qlinear_w16a16(X, 64, 256, 256, W, ctypes.byref(ep), Y, None, 0, None) == -4   # acc_out
     assert L.aria_qpack(16, 32, X, 64, 64, W, None, None) == -4
     assert L.aria_qpack(16, 0, None, 64, 64, W, None, None) == -1
+    # block steps around the linears
+    assert L.aria_layernorm(X, 64, 100, W, S, 1e-5, Y, None) == -2          # W % 8
+    assert L.aria_layernorm(X, 64, 32768, W, S, 1e-5, Y, None) == -2
+    assert L.aria_layernorm(X, 64, 256, W, S, -1.0, Y, None) == -4
+    assert L.aria_layernorm(X, 64, 256, None, S, 1e-5, Y, None) == -1
+    assert L.aria_layernorm(X, 64, 256, W, S + 2, 1e-5, Y, None) == -3
+    assert L.aria_layernorm(X, 64, 256, W, S, 1e-5, X + 512, None) == -7     # partial overlap
+    assert L.aria_attention(X, 64, 96, 2, 32, Y, None) == -4                 # head dim 48
+    assert L.aria_attention(X, 64, 128, 2, 48, Y, None) == -2                # M % seq
+    assert L.aria_attention(None, 64, 128, 2, 32, Y, None) == -1
+    assert L.aria_attention(X, 64, 128, 2, 32, X + 1024, None) == -7
+    assert L.aria_attention(X, 64, 128, 2, 32, Y + 8, None) == -3
     assert L.aria_qlinear_workspace_bytes(9, 64, 64, 64) == 0
     assert L.aria_qlinear_workspace_bytes(0, 64, 40, 64) == 0
 
