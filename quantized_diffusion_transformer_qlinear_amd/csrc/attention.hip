@@ -77,7 +77,8 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
         }
     };
 
-    // scores in the log2 domain: s * (1/sqrt(64)) * log2(e)
+    // exponents in base 2: exp(s / sqrt(64)) = exp2(s * sl2); m is the running
+    // maximum of the raw scores
     const float sl2 = 0.125f * 1.4426950408889634f;
     float m = -INFINITY, lsum = 0.0f;
     v16f ot[2] = {v16f{}, v16f{}};
@@ -97,28 +98,32 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
                 const v8h kf = *reinterpret_cast<const v8h*>(&Ks[cur][32 * jt + lane % 32][16 * t + 8 * hl]);
                 st[jt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[t], st[jt], 0, 0, 0);
             }
-        // online softmax for this lane's query over the block's 64 keys
+        // online softmax for this lane's query over the block's 64 keys, on the
+        // raw scores (the positive scale keeps their order): the scale enters
+        // once, fused into the exponent's argument
+        if (kb + KB > S) {   // the last, partial block: keys past S get no weight
+#pragma unroll
+            for (int jt = 0; jt < 2; jt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    if (kb + 32 * jt + 8 * (r / 4) + 4 * hl + r % 4 >= S) st[jt][r] = -INFINITY;
+        }
         float mb = -INFINITY;
 #pragma unroll
         for (int jt = 0; jt < 2; jt++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = kb + 32 * jt + 8 * (r / 4) + 4 * hl + r % 4;
-                const float sv = st[jt][r];
-                const float s2 = key < S ? sv * sl2 : -INFINITY;
-                st[jt][r] = s2;
-                mb = fmaxf(mb, s2);
-            }
+            for (int r = 0; r < 16; r++) mb = fmaxf(mb, st[jt][r]);
         mb = wave_xor32_max(mb);
         const float mn = fmaxf(m, mb);
-        const float corr = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block (m = -inf)
+        const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);   // 0 on the first block (m = -inf)
+        const float off = -mn * sl2;
         float ps = 0.0f;
         v8h pf[4];
 #pragma unroll
         for (int u = 0; u < 4; u++)
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const float p = __builtin_amdgcn_exp2f(st[u / 2][8 * (u % 2) + e] - mn);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[u / 2][8 * (u % 2) + e], sl2, off));
                 ps += p;
                 pf[u][e] = (half_t)p;
             }
