@@ -292,6 +292,77 @@ def full_block(q, torch, dev, si, blk, packed, reps=20):
             "tops_incl_attention": round((lin_ops + attn_flops) / us_graph / 1e6, 1)}
 
 
+def step_1p2b(q, torch, dev, si, reps=5):
+    """The 1.2B-parameter-scale denoising step: 24 blocks x {QKV 2048->6144,
+    out 2048->2048, MLP-up 2048->8192, MLP-down 8192->2048} = 1,207,959,552
+    linear weights, every linear over the same M = 2048 tokens with a plain
+    fp16 output (the linears are independent; the input of each K is shared).
+    Weights are seeded N(0, 0.02) drawn on the device and packed at 8 and at 4
+    bits (the fp16 copy is released after packing); the step runs at q8
+    (W8A16), q4 (W4A16) and W8A8 on the q8 storage.  Each precision's 96 calls
+    are captured as one graph and replayed: ms per step, aggregate TOPS,
+    algorithmic bytes / time (packed weights + scales + X + Y per linear) and
+    the resident packed footprint (measured allocation and the packed sizes)."""
+    M = si.TOKENS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5000)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    p8, p4 = [], []
+    for _b in range(si.STEP_BLOCKS):
+        for _name, K, N in si.STEP_LAYERS:
+            w = (torch.randn((K, N), generator=gen, device=dev, dtype=torch.float32) * 0.02).half()
+            p8.append((K, N, q.qpack(8, w)))
+            p4.append((K, N, q.qpack(4, w)))
+            del w
+    torch.cuda.synchronize()
+    resident = torch.cuda.memory_allocated() - base
+    packed8 = sum(sum(q.qpack_bytes(8, 0, K, N)) for K, N, _ in p8)
+    packed4 = sum(sum(q.qpack_bytes(4, 32, K, N)) for K, N, _ in p4)
+    fp16_bytes = sum(2 * K * N for K, N, _ in p8)
+    gen.manual_seed(501)
+    xs = {K: torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32).half()
+          for K in sorted({K for _n, K, _N in si.STEP_LAYERS})}
+    ys = {N: torch.empty((M, N), dtype=torch.float16, device=dev) for N in sorted({N for _n, _K, N in si.STEP_LAYERS})}
+    kmax = max(xs)
+    ws = torch.empty(max(q.workspace_bytes(q.ARIA_W8A8, M, kmax, 1), 1), dtype=torch.uint8, device=dev)
+    ops = sum(2.0 * M * K * N for K, N, _ in p8)
+    xy = sum(2.0 * M * (K + N) for K, N, _ in p8)
+    runs = {
+        "q8 (W8A16)": (lambda: [q.qlinear_w8a16(xs[K], *pk, y=ys[N]) for K, N, pk in p8], packed8),
+        "q4 (W4A16)": (lambda: [q.qlinear_w4a16(xs[K], *pk, y=ys[N]) for K, N, pk in p4], packed4),
+        "W8A8 (q8 storage)": (lambda: [q.qlinear_w8a8(xs[K], *pk, y=ys[N], ws=ws) for K, N, pk in p8], packed8),
+    }
+    res = {"linears": len(p8), "weights": sum(K * N for K, N, _ in p8), "ops_per_step": ops,
+           "resident_bytes": {"fp16 (released)": fp16_bytes, "q8": packed8, "q4": packed4,
+                              "allocated_q8_plus_q4": resident}}
+    for name, (fn, wbytes) in runs.items():
+        fn()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            fn()
+            with torch.cuda.graph(g, stream=st):
+                fn()
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(e) / reps
+        res[name] = {"ms_per_step": round(ms, 3), "tops": round(ops / ms / 1e9, 1),
+                     "GB/s": round((wbytes + xy) / ms / 1e6, 1)}
+        del g
+    del p8, p4, xs, ys, ws
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,7 +371,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the small-M streaming and precision-ladder measurements")
+                    help="skip the small-M streaming, precision-ladder, full-block and 1.2B-step measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -471,6 +542,7 @@ def main():
         out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
         out["precision_ladder_1536x6144"] = precision_ladder(q, torch, dev, lin2, x3)
         out["dit_block_full_m2048"] = full_block(q, torch, dev, si, blk, packed)
+        out["step_1p2b_m2048"] = step_1p2b(q, torch, dev, si)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
     print(json.dumps(out), flush=True)
