@@ -24,13 +24,21 @@ FLAGS = [
 ]
 
 
+# per-source additions: the attention kernel does VALU work (softmax, rescaling)
+# on its MFMA results every key block, so its accumulators are kept in
+# ordinary VGPRs (the VGPR form of MFMA) instead of accumulation registers that
+# every such access would first have to copy out
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    r = subprocess.run([HIPCC, *FLAGS, "-c", src, "-o", obj], capture_output=True, text=True)
+    extra = EXTRA.get(os.path.basename(src), [])
+    r = subprocess.run([HIPCC, *FLAGS, *extra, "-c", src, "-o", obj], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     return obj

@@ -17,6 +17,8 @@
 // transposed), the next block's loads are in flight during the current
 // block's matrix work, one barrier per block.  Scores, the softmax and the
 // accumulators are fp32; P and the output are rounded to fp16.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +30,10 @@ constexpr int HD = 64;        // head dimension
 constexpr int KB = 64;        // keys per block
 constexpr int QW = 4;         // waves per workgroup (32 queries each)
 constexpr int KROW = HD + 8;  // K rows in LDS, halves (16-byte pad)
-constexpr int VROW = KB + 8;  // V^T rows in LDS, halves
+constexpr int VROW = KB + 4;  // V^T rows in LDS, halves (136 bytes: the 8-byte runs of the
+                              // V stores and of the fragment reads both spread over all banks)
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0), expcnt and lgkmcnt(0)
+constexpr int kWaitVm0 = 0x0070;
 
 __device__ __forceinline__ float wave_xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, WAVE)); }
 __device__ __forceinline__ float wave_xor32_sum(float v) { return v + __shfl_xor(v, 32, WAVE); }
@@ -46,7 +51,50 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
     const int64_t row0 = (int64_t)seq * S;              // first row of the sequence
     const rsrc_t rq = make_rsrc(qkv + row0 * ld, (uint32_t)S * (uint32_t)ld * 2);
 
-    // Q^T fragments (B operand): lane = query q0 + lane % 32, d = 16 t + 8 hl .. +7
+    // Cooperative K / V block loads, 16-byte chunks, four per thread; waves 0-1
+    // fetch V, waves 2-3 fetch K (a wave-uniform split).  A V thread takes
+    // four consecutive keys 4j .. 4j+3 of one 8-column piece p, so that it can
+    // write V^T as 8-byte runs of four keys: Vt[8p + e][4j .. 4j+3].  A K thread
+    // takes chunks c = t + 128 i (key c / 8, piece c % 8), stored row-major.
+    const bool vthread = wave < 2;
+    const int ct = vthread ? tid : tid - 2 * WAVE;   // 0 .. 127 within the role
+    v4i rkv[4];
+    auto load_kv = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int key, col;
+            if (vthread) key = 4 * (ct / 8) + i, col = 2 * W + h * HD + (ct % 8) * 8;
+            else key = (ct + 128 * i) / 8, col = W + h * HD + ((ct + 128 * i) % 8) * 8;
+            const int j = kb + key;
+            rkv[i] = buf_load16(rq, j < S ? ((uint32_t)j * ld + col) * 2 : OOB);
+        }
+    };
+    auto store_kv = [&](int buf) {
+        if (vthread) {
+            const int j4 = 4 * (ct / 8), p8 = (ct % 8) * 8;
+            v8h v[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[i] = __builtin_bit_cast(v8h, rkv[i]);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const v2h lo = {v[0][e], v[1][e]}, hi = {v[2][e], v[3][e]};
+                *reinterpret_cast<v2u*>(&Vt[buf][p8 + e][j4]) = v2u{__builtin_bit_cast(u32, lo), __builtin_bit_cast(u32, hi)};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int c = ct + 128 * i;
+                *reinterpret_cast<v4i*>(&Ks[buf][c / 8][(c % 8) * 8]) = rkv[i];
+            }
+        }
+    };
+
+    // Block 0's loads first, then Q^T fragments (B operand: lane = query
+    // q0 + lane % 32, d = 16 t + 8 hl .. +7); every load before the loop has
+    // landed before block 1 is requested, so no load is still pending at the
+    // loop head (one that were would make each iteration wait for the
+    // prefetched block as well).
+    load_kv(0);
     v8h qf[4];
     {
         const int q = q0 + lane % 32;
@@ -54,40 +102,27 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
         for (int t = 0; t < 4; t++)
             qf[t] = __builtin_bit_cast(v8h, buf_load16(rq, q < S ? ((uint32_t)q * ld + h * HD + 16 * t + 8 * hl) * 2 : OOB));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    store_kv(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // cooperative K / V block loads: 512 chunks of 16 bytes each, 2 + 2 per thread
-    v4i rk[2], rv[2];
-    auto load_kv = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int c = tid + i * QW * WAVE, key = c / 8, piece = c % 8, j = kb + key;
-            const uint32_t base = (uint32_t)j * ld + h * HD + piece * 8;
-            rk[i] = buf_load16(rq, j < S ? (base + W) * 2 : OOB);
-            rv[i] = buf_load16(rq, j < S ? (base + 2 * W) * 2 : OOB);
-        }
-    };
-    auto store_kv = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int c = tid + i * QW * WAVE, key = c / 8, piece = c % 8;
-            *reinterpret_cast<v4i*>(&Ks[buf][key][piece * 8]) = rk[i];
-            const v8h v = __builtin_bit_cast(v8h, rv[i]);
-#pragma unroll
-            for (int e = 0; e < 8; e++) Vt[buf][piece * 8 + e][key] = v[e];
-        }
-    };
-
-    // exponents in base 2: exp(s / sqrt(64)) = exp2(s * sl2); m is the running
-    // maximum of the raw scores
+    // Exponents in base 2: exp(s / sqrt(64)) = exp2(s * sl2).  m is the
+    // reference the exponents are taken against (raw score units): it is
+    // raised to the block maximum only when that exceeds it by more than
+    // 2^kHeadroom in the exponentiated domain, so the rescaling of the sums and
+    // accumulators is skipped for most blocks; P = exp2((s - m) sl2) stays
+    // below 2^kHeadroom, well inside fp16.  The result does not depend on the
+    // reference (it cancels in O / sum).
+    constexpr float kHeadroom = 8.0f;
     const float sl2 = 0.125f * 1.4426950408889634f;
     float m = -INFINITY, lsum = 0.0f;
     v16f ot[2] = {v16f{}, v16f{}};
-    const int nkb = (S + KB - 1) / KB;
-    load_kv(0);
-    store_kv(0);
+    const int nkb = (S + KB - 1) / KB, nfull = S / KB;
     if (nkb > 1) load_kv(KB);
     __syncthreads();
-    for (int b = 0; b < nkb; b++) {
+    auto block = [&](int b, auto masked_c) {
+        constexpr bool masked = decltype(masked_c)::value;
         const int cur = b & 1, kb = b * KB;
         // S^T tiles: keys 32 jt + (row), queries (column = lane % 32)
         v16f st[2] = {v16f{}, v16f{}};
@@ -98,25 +133,30 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
                 const v8h kf = *reinterpret_cast<const v8h*>(&Ks[cur][32 * jt + lane % 32][16 * t + 8 * hl]);
                 st[jt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[t], st[jt], 0, 0, 0);
             }
-        // online softmax for this lane's query over the block's 64 keys, on the
-        // raw scores (the positive scale keeps their order): the scale enters
-        // once, fused into the exponent's argument
-        if (kb + KB > S) {   // the last, partial block: keys past S get no weight
+        if constexpr (masked) {   // the partial last block: keys past S get no weight
 #pragma unroll
             for (int jt = 0; jt < 2; jt++)
 #pragma unroll
                 for (int r = 0; r < 16; r++)
                     if (kb + 32 * jt + 8 * (r / 4) + 4 * hl + r % 4 >= S) st[jt][r] = -INFINITY;
         }
+        // online softmax for this lane's query over the block's 64 keys
         float mb = -INFINITY;
 #pragma unroll
         for (int jt = 0; jt < 2; jt++)
 #pragma unroll
             for (int r = 0; r < 16; r++) mb = fmaxf(mb, st[jt][r]);
         mb = wave_xor32_max(mb);
-        const float mn = fmaxf(m, mb);
-        const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);   // 0 on the first block (m = -inf)
-        const float off = -mn * sl2;
+        const bool raise = (mb - m) * sl2 > kHeadroom;   // always on the first block (m = -inf)
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float mn = raise ? mb : m;
+            const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);   // 1 if not raised, 0 on the first block
+            lsum *= corr;
+#pragma unroll
+            for (int dt = 0; dt < 2; dt++) ot[dt] *= corr;
+            m = mn;
+        }
+        const float off = -m * sl2;
         float ps = 0.0f;
         v8h pf[4];
 #pragma unroll
@@ -127,10 +167,7 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
                 ps += p;
                 pf[u][e] = (half_t)p;
             }
-        lsum = lsum * corr + wave_xor32_sum(ps);
-        m = mn;
-#pragma unroll
-        for (int dt = 0; dt < 2; dt++) ot[dt] *= corr;
+        lsum += wave_xor32_sum(ps);
         // O^T += V^T P^T over the block's 4 k-steps of 16 keys; register e of
         // P^T step u is key 16 u + 4 hl + 8 (e / 4) + e % 4
 #pragma unroll
@@ -150,7 +187,9 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
             if (b + 2 < nkb) load_kv(kb + 2 * KB);
         }
         __syncthreads();
-    }
+    };
+    for (int b = 0; b < nfull; b++) block(b, std::false_type{});
+    if (nfull < nkb) block(nfull, std::true_type{});
 
     // out[query][h*64 + d] = O^T[d][query] / sum; register r of tile dt is
     // d = 32 dt + 8 (r / 4) + 4 hl + r % 4: four consecutive d per 8-byte store
