@@ -9,14 +9,16 @@
 // of 4 waves owns 128 queries of one (sequence, head); each wave keeps its 32
 // queries' Q fragments in registers and computes S^T = K Q^T, so that a lane
 // holds the scores of ONE query (column l % 32) for 32 keys: the running max
-// and sum of the online softmax need one cross-lane exchange per key block
-// instead of a reduction over 32 lanes.  P^T (fp16) is fed straight from the
-// score registers as the B operand of O^T += V^T P^T; the key order that the
-// score layout implies is matched by how V^T is read from LDS.  Key blocks of
-// 64 are double-buffered in LDS (K row-major with a 16-byte row pad, V stored
-// transposed), the next block's loads are in flight during the current
-// block's matrix work, one barrier per block.  Scores, the softmax and the
-// accumulators are fp32; P and the output are rounded to fp16.
+// needs one cross-lane exchange per key block instead of a reduction over 32
+// lanes.  P^T (fp16) is fed straight from the score registers as the B
+// operand of O^T += V^T P^T (the key order that the score layout implies is
+// matched by how V^T is read from LDS), and of a ones-tile product that yields
+// the softmax denominators on the matrix unit too.  Key blocks of 64 are
+// double-buffered in LDS (K row-major with a 16-byte row pad, V transposed
+// with 8-byte runs of four keys), the next block's loads are in flight during
+// the current block's matrix work, one barrier per block.  Scores, the
+// softmax statistics and the accumulators are fp32 (kept in VGPRs: the
+// softmax touches them every block); P and the output are rounded to fp16.
 #include <type_traits>
 
 #include "common.h"
@@ -36,7 +38,6 @@ constexpr int VROW = KB + 4;  // V^T rows in LDS, halves (136 bytes: the 8-byte 
 constexpr int kWaitVm0 = 0x0070;
 
 __device__ __forceinline__ float wave_xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, WAVE)); }
-__device__ __forceinline__ float wave_xor32_sum(float v) { return v + __shfl_xor(v, 32, WAVE); }
 
 }  // namespace
 
@@ -116,8 +117,15 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
     // reference (it cancels in O / sum).
     constexpr float kHeadroom = 8.0f;
     const float sl2 = 0.125f * 1.4426950408889634f;
-    float m = -INFINITY, lsum = 0.0f;
+    float m = -INFINITY;
     v16f ot[2] = {v16f{}, v16f{}};
+    // the softmax denominators come from the matrix unit as well: a 32-row
+    // tile of ones times P^T gives every row the column sums of P^T, i.e.
+    // each query's sum of the (fp16-rounded) weights that enter O
+    v16f ls = {};
+    v8h ones;
+#pragma unroll
+    for (int e = 0; e < 8; e++) ones[e] = (half_t)1.0f;
     const int nkb = (S + KB - 1) / KB, nfull = S / KB;
     if (nkb > 1) load_kv(KB);
     __syncthreads();
@@ -151,23 +159,18 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
         if (__builtin_amdgcn_ballot_w64(raise)) {
             const float mn = raise ? mb : m;
             const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);   // 1 if not raised, 0 on the first block
-            lsum *= corr;
+            ls *= corr;
 #pragma unroll
             for (int dt = 0; dt < 2; dt++) ot[dt] *= corr;
             m = mn;
         }
         const float off = -m * sl2;
-        float ps = 0.0f;
         v8h pf[4];
 #pragma unroll
         for (int u = 0; u < 4; u++)
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[u / 2][8 * (u % 2) + e], sl2, off));
-                ps += p;
-                pf[u][e] = (half_t)p;
-            }
-        lsum += wave_xor32_sum(ps);
+            for (int e = 0; e < 8; e++)
+                pf[u][e] = (half_t)__builtin_amdgcn_exp2f(__builtin_fmaf(st[u / 2][8 * (u % 2) + e], sl2, off));
         // O^T += V^T P^T over the block's 4 k-steps of 16 keys; register e of
         // P^T step u is key 16 u + 4 hl + 8 (e / 4) + e % 4
 #pragma unroll
@@ -180,6 +183,8 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
                 const v8h vf = __builtin_bit_cast(v8h, v4u{lo[0], lo[1], hi[0], hi[1]});
                 ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[u], ot[dt], 0, 0, 0);
             }
+#pragma unroll
+        for (int u = 0; u < 4; u++) ls = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pf[u], ls, 0, 0, 0);
         // the next block: stored into the other buffer (free since the last
         // barrier), the one after it requested
         if (b + 1 < nkb) {
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(QW * WAVE) void attention_kernel(const half_t* __re
     // d = 32 dt + 8 (r / 4) + 4 hl + r % 4: four consecutive d per 8-byte store
     const int q = q0 + lane % 32;
     if (q < S) {
-        const float inv = 1.0f / lsum;
+        const float inv = 1.0f / ls[0];
         half_t* orow = out + (row0 + q) * W + h * HD;
 #pragma unroll
         for (int dt = 0; dt < 2; dt++)
