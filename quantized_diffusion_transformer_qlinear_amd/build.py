@@ -24,11 +24,13 @@ FLAGS = [
 ]
 
 
-# per-source additions: the attention kernel does VALU work (softmax, rescaling)
-# on its MFMA results every key block, so its accumulators are kept in
-# ordinary VGPRs (the VGPR form of MFMA) instead of accumulation registers that
-# every such access would first have to copy out
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source additions: MFMA accumulators in ordinary VGPRs (the VGPR form of
+# MFMA).  The attention kernel does VALU work (softmax, rescaling) on its MFMA
+# results every key block, which accumulation registers would first have to
+# copy out; the 4-wave GEMM tiles otherwise get accumulation registers on top
+# of their VGPRs and drop to one wave per SIMD.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"attention.hip": VGPR_FORM, "gemm_tiled.hip": VGPR_FORM}
 
 
 def sources():

@@ -15,13 +15,16 @@
 // (v_mfma_i32_32x32x32_i8 or v_mfma_f32_32x32x16_f16).  Both operands live in
 // LDS as rows of 128 bytes (128 int8 k or 64 fp16 k) plus a 16-byte pad that
 // spreads the 32 rows of an operand fragment over all banks; a K-step is 4
-// MFMA sub-steps in every mode.  The next tile is fetched two K-steps ahead
-// into registers with bounds-checked buffer loads (rows past M/N and k past K
-// read as zero), and its decode + LDS store is split over the 4 sub-steps of
+// MFMA sub-steps in every mode.  Tiles are fetched two K-steps ahead (three
+// for 4-wave tiles) into registers with bounds-checked buffer loads (rows past
+// M/N and k past K read as zero), and the decode + LDS store of the next one
+// is split over the 4 sub-steps of
 // the current K-step so that it overlaps the matrix work; one barrier per
 // K-step.  Packed weights are decoded in registers: int8 -> fp16 and nibble
 // -> fp16 by building the fp16 pattern 0x6400 | u (= 1024 + u) and
 // subtracting the bias, two values per packed-half instruction.
+#include <type_traits>
+
 #include "common.h"
 #include "decode.h"
 #include "kernels.h"
@@ -96,58 +99,63 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     const int G = K / 32;
 
     // per-thread chunk coordinates (fixed across K-steps)
-    v4i RA[LA], RB[LB > 0 ? LB : 1];
-    half_t RS[LB > 0 ? LB : 1];
+    // 4-wave tiles (two workgroups per CU) keep the next-but-one tile in a
+    // second register set, so a load has a whole K-step to land; the 8-wave
+    // tiles lack the registers for it and hide latency with their second wave
+    // per SIMD instead
+    constexpr int NSET = WM * WN == 4 ? 2 : 1;
+    v4i RA[NSET][LA], RB[NSET][LB > 0 ? LB : 1];
+    half_t RS[NSET][LB > 0 ? LB : 1];
 
-    auto load_a = [&](int kt, int i) {
+    auto load_a = [&](int kt, int i, int set) {
         const int c = tid + i * NT, row = c / 8, ch = c % 8;
         const int k = kt * T::KSTEP + ch * (16 / T::AEB);
         const uint32_t off = (uint32_t)(m0 + row) * (uint32_t)K * T::AEB + (uint32_t)k * T::AEB;
-        RA[i] = buf_load16(ra, k < K && m0 + row < M ? off : OOB);
+        RA[set][i] = buf_load16(ra, k < K && m0 + row < M ? off : OOB);
     };
     // threads past the last B chunk (NB not a multiple of 256) redo chunk c % NB:
     // the same bytes land at the same LDS address, which keeps the loop branch-free
-    auto load_b = [&](int kt, int i) {
+    auto load_b = [&](int kt, int i, int set) {
         const int c = (tid + i * NT) % NB, row = c / T::BCH, ch = c % T::BCH;
         const int k = kt * T::KSTEP + ch * T::KPB;
         const bool in = k < K && n0 + row < N;
         const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : MODE == 3 ? 2 * k : k);
-        RB[i] = buf_load16(rb, in ? off : OOB);
-        if (MODE == 2) RS[i] = S[(int64_t)min(n0 + row, N - 1) * G + min(k, K - 32) / 32];
+        RB[set][i] = buf_load16(rb, in ? off : OOB);
+        if (MODE == 2) RS[set][i] = S[(int64_t)min(n0 + row, N - 1) * G + min(k, K - 32) / 32];
     };
-    auto store_a = [&](int buf, int i) {
+    auto store_a = [&](int buf, int i, int set) {
         const int c = tid + i * NT, row = c / 8, ch = c % 8;
-        *reinterpret_cast<v4i*>(&lds[buf][row * ROWB + ch * 16]) = RA[i];
+        *reinterpret_cast<v4i*>(&lds[buf][row * ROWB + ch * 16]) = RA[set][i];
     };
-    auto store_b = [&](int buf, int i) {
+    auto store_b = [&](int buf, int i, int set) {
         const int c = (tid + i * NT) % NB;
         const int row = c / T::BCH, ch = c % T::BCH;
         char* dst = &lds[buf][(BM + row) * ROWB + ch * (T::KPB * 2 / (MODE == 0 ? 2 : 1))];
         if constexpr (MODE == 0 || MODE == 3) {
-            *reinterpret_cast<v4i*>(dst) = RB[i];
+            *reinterpret_cast<v4i*>(dst) = RB[set][i];
         } else if constexpr (MODE == 1) {
             v4i lo, hi;
-            dec8(RB[i], lo, hi);
+            dec8(RB[set][i], lo, hi);
             reinterpret_cast<v4i*>(dst)[0] = lo;
             reinterpret_cast<v4i*>(dst)[1] = hi;
         } else {
             v4i o[4];
-            dec4(RB[i], RS[i], o);
+            dec4(RB[set][i], RS[set][i], o);
 #pragma unroll
             for (int q = 0; q < 4; q++) reinterpret_cast<v4i*>(dst)[q] = o[q];
         }
     };
-    auto load_part = [&](int kt, int p) {
+    auto load_part = [&](int kt, int p, int set) {
 #pragma unroll
-        for (int i = p; i < LA; i += 4) load_a(kt, i);
+        for (int i = p; i < LA; i += 4) load_a(kt, i, set);
 #pragma unroll
-        for (int i = p; i < LB; i += 4) load_b(kt, i);
+        for (int i = p; i < LB; i += 4) load_b(kt, i, set);
     };
-    auto store_part = [&](int buf, int p) {
+    auto store_part = [&](int buf, int p, int set) {
 #pragma unroll
-        for (int i = p; i < LA; i += 4) store_a(buf, i);
+        for (int i = p; i < LA; i += 4) store_a(buf, i, set);
 #pragma unroll
-        for (int i = p; i < LB; i += 4) store_b(buf, i);
+        for (int i = p; i < LB; i += 4) store_b(buf, i, set);
     };
 
     typename T::acc_t acc[FM][FN];
@@ -158,11 +166,15 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
 
     const int nk = (K + T::KSTEP - 1) / T::KSTEP;
 #pragma unroll
-    for (int p = 0; p < 4; p++) load_part(0, p);
+    for (int p = 0; p < 4; p++) load_part(0, p, 0);
 #pragma unroll
-    for (int p = 0; p < 4; p++) store_part(0, p);
+    for (int p = 0; p < 4; p++) store_part(0, p, 0);
 #pragma unroll
-    for (int p = 0; p < 4; p++) load_part(1, p);
+    for (int p = 0; p < 4; p++) load_part(1, p, NSET - 1);
+    if constexpr (NSET == 2) {
+#pragma unroll
+        for (int p = 0; p < 4; p++) load_part(2, p, 0);
+    }
     __syncthreads();
 
     const int arow = (wm * WTM + lane % 32) * ROWB + (lane / 32) * 16;
@@ -176,7 +188,10 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     };
     // The loop body has no branches: the last K-steps load past K (zero-fill,
     // no memory traffic) and store into the idle buffer, which nothing reads.
-    for (int kt = 0; kt < nk; kt++) {
+    // Register set `set` holds tile kt + 1 (stored during K-step kt); with two
+    // sets the tile after the next-but-one is requested into it once stored.
+    auto kstep = [&](int kt, auto set_c) {
+        constexpr int set = decltype(set_c)::value;
         const int cur = kt & 1;
         const char* L = lds[cur];
         read_frags(L, 0, 0);
@@ -194,10 +209,23 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                                                                            __builtin_bit_cast(v8h, fb[p & 1][j]),
                                                                            acc[i][j], 0, 0, 0);
                 }
-            store_part(cur ^ 1, p);
-            load_part(kt + 2, p);
+            store_part(cur ^ 1, p, set);
+            load_part(kt + 1 + NSET, p, set);
+            // keep each part's loads in its sub-step (the scheduler would
+            // otherwise sink them all to the end of the K-step)
+            if constexpr (NSET == 2) __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
+    };
+    if constexpr (NSET == 2) {
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            kstep(kt, std::integral_constant<int, 1>{});
+            kstep(kt + 1, std::integral_constant<int, 0>{});
+        }
+        if (kt < nk) kstep(kt, std::integral_constant<int, 1>{});
+    } else {
+        for (int kt = 0; kt < nk; kt++) kstep(kt, std::integral_constant<int, 0>{});
     }
 
     // Epilogue.  Each wave stages one 32-row block-row of its raw accumulators
@@ -337,19 +365,23 @@ struct TileCfg {
     float eff[4];  // sustained throughput of one full wave of such tiles, per mode (relative units)
 };
 
-// Candidate macro tiles with their measured per-tile efficiency on MI355X
-// (throughput of a whole number of tile waves at M = 2048, K = 2048, by mode
-// W8A8 / W8A16 / W4A16 / W16A16).  The picker minimises
+// Candidate macro tiles with their measured per-tile efficiency on MI355X, by
+// mode W8A8 / W8A16 / W4A16 / W16A16: for each tile, waves x BM x BN x K / time
+// (relative units), the median over eight layer shapes at M = 2048 (the DiT
+// block's four linears at width 1536 and the four of the 1.2B-scale step at
+// width 2048), with two W8A16 / W16A16 entries of 128x128 nudged so that the
+// picker's choice is within 1 % of the fastest tile on those shapes.  The
+// picker minimises
 //   ceil(tiles / CUs) * BM * BN / eff
 // i.e. it trades CU fill (whole waves of tiles) against per-tile efficiency;
 // 8-wave workgroups put two waves on every SIMD so one can issue while the
 // other waits on LDS or memory.
 constexpr TileCfg kTiles[] = {
-    {256, 256, 4, 2, {1845.f, 1248.f, 1176.f, 1310.f}}, {256, 192, 4, 2, {1545.f, 970.f, 893.f, 1048.f}},
-    {256, 128, 4, 2, {1599.f, 1015.f, 856.f, 1066.f}},  {128, 256, 2, 4, {1605.f, 1008.f, 899.f, 1048.f}},
-    {128, 192, 2, 2, {1168.f, 744.f, 611.f, 818.f}},   {128, 128, 2, 2, {1347.f, 795.f, 731.f, 906.f}},
-    {64, 192, 2, 2, {1211.f, 706.f, 516.f, 741.f}},    {128, 64, 2, 2, {1160.f, 672.f, 531.f, 699.f}},
-    {64, 128, 2, 2, {1163.f, 619.f, 559.f, 656.f}},    {64, 64, 2, 2, {1097.f, 570.f, 358.f, 570.f}}};
+    {256, 256, 4, 2, {4044.f, 2467.f, 2409.f, 2635.f}}, {256, 192, 4, 2, {3838.f, 2229.f, 2125.f, 2375.f}},
+    {256, 128, 4, 2, {3225.f, 2040.f, 1670.f, 1994.f}}, {128, 256, 2, 4, {3421.f, 1991.f, 1797.f, 2055.f}},
+    {128, 192, 2, 2, {2419.f, 1556.f, 1328.f, 1671.f}}, {128, 128, 2, 2, {2764.f, 1899.f, 1444.f, 1844.f}},
+    {64, 192, 2, 2, {2333.f, 1383.f, 1007.f, 1358.f}},  {128, 64, 2, 2, {2370.f, 1318.f, 1074.f, 1358.f}},
+    {64, 128, 2, 2, {2361.f, 1323.f, 1138.f, 1355.f}},  {64, 64, 2, 2, {2167.f, 1163.f, 828.f, 1156.f}}};
 
 int num_cus() {
     static int cus = 0;
