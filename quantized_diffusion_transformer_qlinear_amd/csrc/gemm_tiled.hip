@@ -18,11 +18,14 @@
 // MFMA sub-steps in every mode.  Tiles are fetched two K-steps ahead (three
 // for 4-wave tiles) into registers with bounds-checked buffer loads (rows past
 // M/N and k past K read as zero), and the decode + LDS store of the next one
-// is split over the 4 sub-steps of
-// the current K-step so that it overlaps the matrix work; one barrier per
-// K-step.  Packed weights are decoded in registers: int8 -> fp16 and nibble
-// -> fp16 by building the fp16 pattern 0x6400 | u (= 1024 + u) and
-// subtracting the bias, two values per packed-half instruction.
+// is split over the first 3 sub-steps of the current K-step so that it
+// overlaps the matrix work.  The one barrier per K-step comes after the third
+// sub-step: the next tile is then complete in LDS, and its first fragments are
+// read while the last sub-step's MFMAs run (a barrier at the end of the K-step
+// left every wave waiting on those reads with nothing to issue).  Packed
+// weights are decoded in registers: int8 -> fp16 and nibble -> fp16 by
+// building the fp16 pattern 0x6400 | u (= 1024 + u) and subtracting the bias,
+// two values per packed-half instruction.
 #include <type_traits>
 
 #include "common.h"
@@ -190,14 +193,17 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     // no memory traffic) and store into the idle buffer, which nothing reads.
     // Register set `set` holds tile kt + 1 (stored during K-step kt); with two
     // sets the tile after the next-but-one is requested into it once stored.
+    // The barrier after sub-step 2 publishes tile kt + 1; every wave has read
+    // all fragments of tile kt by then (sub-step 3's were read during sub-step
+    // 2), so the next K-step may overwrite tile kt's buffer.
     auto kstep = [&](int kt, auto set_c) {
         constexpr int set = decltype(set_c)::value;
         const int cur = kt & 1;
         const char* L = lds[cur];
-        read_frags(L, 0, 0);
 #pragma unroll
         for (int p = 0; p < 4; p++) {
             if (p < 3) read_frags(L, p + 1, (p + 1) & 1);
+            else read_frags(lds[cur ^ 1], 0, 0);   // the next tile's first sub-step: visible since the barrier
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -209,14 +215,19 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                                                                            __builtin_bit_cast(v8h, fb[p & 1][j]),
                                                                            acc[i][j], 0, 0, 0);
                 }
-            store_part(cur ^ 1, p, set);
-            load_part(kt + 1 + NSET, p, set);
-            // keep each part's loads in its sub-step (the scheduler would
-            // otherwise sink them all to the end of the K-step)
+            if (p < 3) {
+                store_part(cur ^ 1, p, set);
+                load_part(kt + 1 + NSET, p, set);
+                if (p == 2) {
+                    store_part(cur ^ 1, 3, set);
+                    load_part(kt + 1 + NSET, 3, set);
+                    __syncthreads();
+                }
+            }
             if constexpr (NSET == 2) __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
     };
+    read_frags(lds[0], 0, 0);
     if constexpr (NSET == 2) {
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
