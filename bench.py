@@ -14,9 +14,10 @@ The step is captured once into a HIP graph and the timed region replays it K
 times (the pages replay the denoising loop as one captured graph; the C-ABI
 enqueues without allocating or synchronising, so it captures as-is).  The
 printed value is the aggregate contraction throughput of the step in TOPS
-(2*M*K*N per linear; int8 and fp16 operations counted alike).  A second,
-eager pass times every call with events for the per-call breakdown and the
-dominant kernel's roofline.
+(2*M*K*N per linear; int8 and fp16 operations counted alike).  For the
+per-call breakdown and the dominant kernel's roofline every call is then
+captured alone (ten launches in one graph) and replayed between events on the
+replay stream: kernel time plus graph launch gaps, no host time.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--eager] [--no-extras] [--copy-calibration]
@@ -130,6 +131,29 @@ def cpu_baseline(inputs, budget_s=12.0):
                       f"({ops / 1e9:.1f} G ops in {dt:.1f} s; plain C fp64/int64 oracle, OpenMP, {cpu})"}
 
 
+def graph_us(torch, fn, n=10, reps=5):
+    """Microseconds per call of fn: n calls captured in one HIP graph on a side
+    stream, replayed `reps` times between two events on that stream (the
+    kernels' own time plus graph launch gaps; no host time)."""
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn()
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(n):
+                fn()
+        g.replay()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        e.record()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(e) * 1e3 / (reps * n)
+
+
 def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
     """W4A16 at small M, where the layer is bound by streaming its 4-bit weights:
     the same 1536x6144 layer as `copies` distinct packed copies (1.06 GB, past
@@ -207,7 +231,7 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
 def precision_ladder(q, torch, dev, lin2, x_small, reps=20):
     """The pages' precision ladder (fp16 / q8 / W8A8 / q4) restated for one
     1536 -> 6144 layer (bias + GELU) at M = 2048 and at M = 16: microseconds
-    per call, eager launches timed with events (weights resident)."""
+    per call, graph-replayed (weights resident)."""
     K, N = lin2.w.shape
     wd = torch.from_numpy(lin2.w).to(dev)
     packs = {16: q.qpack(16, wd), 8: q.qpack(8, wd), 4: q.qpack(4, wd)}
@@ -226,16 +250,7 @@ def precision_ladder(q, torch, dev, lin2, x_small, reps=20):
         }
         row = {}
         for name, fn in calls.items():
-            for _ in range(3):
-                fn()
-            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record()
-            for _ in range(reps):
-                fn()
-            e.record()
-            torch.cuda.synchronize()
-            us = a.elapsed_time(e) / reps * 1e3
+            us = graph_us(torch, fn)
             row[name] = {"us": round(us, 2), "tops": round(2.0 * M * K * N / us / 1e6, 1)}
         res[f"M={M}"] = row
     return res
@@ -245,7 +260,7 @@ def full_block(q, torch, dev, si, blk, packed, reps=20):
     """The W8A8 DiT block with its attention core and pre-norms (LN1, QKV,
     attention over 2 x 1024 tokens with 24 heads of 64, out + residual, LN2,
     MLP-up + GELU, MLP-down + residual + alpha*d) at M = 2048: graph-replayed
-    microseconds per block and an eager per-stage breakdown."""
+    microseconds per block and a per-stage breakdown (each stage alone, graph-replayed)."""
     from quantized_diffusion_transformer_qlinear_amd.chain import DitBlockFullW8A8
     norms = si.dit_block_norms()
     ln1 = tuple(torch.from_numpy(a).to(dev) for a in norms["ln1"])
@@ -254,7 +269,6 @@ def full_block(q, torch, dev, si, blk, packed, reps=20):
     chain = DitBlockFullW8A8(packed, ln1, ln2, si.TOKENS, si.WIDTH, si.MLP, si.HEADS, si.SEQ,
                              steer_dir=torch.from_numpy(blk["d"]).to(dev), steer_alpha=alpha)
     h = torch.from_numpy(blk["h"]).to(dev)
-    names = ["ln1", "qkv", "attention", "out", "ln2", "up", "down"]
     for _ in range(3):
         chain.run(h)
     g = torch.cuda.CUDAGraph()
@@ -273,20 +287,12 @@ def full_block(q, torch, dev, si, blk, packed, reps=20):
     e.record()
     torch.cuda.synchronize()
     us_graph = a.elapsed_time(e) / reps * 1e3
-    per = {n: 0.0 for n in names}
-    for _ in range(reps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-        evs[0].record()
-        for i, _n in enumerate(chain.stages(h)):
-            evs[i + 1].record()
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            per[n] += evs[i].elapsed_time(evs[i + 1]) * 1e3 / reps
+    per = {n: graph_us(torch, fn) for n, fn in chain.calls(h)}
     W, F, M = si.WIDTH, si.MLP, si.TOKENS
     lin_ops = 2.0 * M * W * (3 * W + W + F) + 2.0 * M * F * W
     attn_flops = 2 * 2.0 * M * si.SEQ * W          # QK^T and PV over each sequence
     return {"us_per_block_graph": round(us_graph, 2),
-            "stages_us_eager": {n: round(v, 2) for n, v in per.items()},
+            "stages_us_graph": {n: round(v, 2) for n, v in per.items()},
             "attention_tflops": round(attn_flops / per["attention"] / 1e6, 1),
             "ops_per_block": {"linears": lin_ops, "attention": attn_flops},
             "tops_incl_attention": round((lin_ops + attn_flops) / us_graph / 1e6, 1)}
@@ -421,20 +427,11 @@ def main():
 
     names = ["w8a8.qkv", "attention(copy)", "w8a8.out", "w8a8.up", "w8a8.down", "w8a16.up", "w4a16"]
 
-    def step(evs=None):
-        i = 0
-        if evs is not None:
-            evs[0].record()
+    def step():
         for _ in chain.stages(h):
-            i += 1
-            if evs is not None:
-                evs[i].record()
+            pass
         q.qlinear_w8a16(x2, wq2, sw2, y=y2, bias=b2, gelu=True)
-        if evs is not None:
-            evs[6].record()
         q.qlinear_w4a16(x3d, wq3, sg3, y=y3)
-        if evs is not None:
-            evs[7].record()
 
     for _ in range(args.warmup):
         step()
@@ -469,13 +466,12 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # eager pass with events between the calls: per-call durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
-    for s_ in range(args.steps):
-        step(evs[s_])
-    torch.cuda.synchronize()
-    per = {n: sum(evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)) / args.steps * 1e3
-           for i, n in enumerate(names)}  # us per call
+    # per-call durations: each call alone, graph-replayed on its own stream
+    call_fns = dict(zip(["w8a8.qkv", "attention(copy)", "w8a8.out", "w8a8.up", "w8a8.down"],
+                        [fn for _n, fn in chain.calls(h)]))
+    call_fns["w8a16.up"] = lambda: q.qlinear_w8a16(x2, wq2, sw2, y=y2, bias=b2, gelu=True)
+    call_fns["w4a16"] = lambda: q.qlinear_w4a16(x3d, wq3, sg3, y=y3)
+    per = {n: graph_us(torch, call_fns[n]) for n in names}  # us per call
 
     copy_us = None
     if args.copy_calibration:

@@ -52,20 +52,26 @@ class DitBlockW8A8:
         need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, 1) for k in (width, mlp))
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
+    def calls(self, h, stream=None):
+        """The stages as (name, callable) pairs, in order; each call enqueues one
+        stage on the stream (re-running one alone recomputes it from the
+        buffers the previous stage left)."""
+        p = self.packed
+        return [
+            ("qkv", lambda: B.qlinear_w8a8(h, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)),
+            ("attention", lambda: copy_columns(self.a, self.qkv, 2 * self.width, self.width, stream)),
+            ("out", lambda: B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)),
+            ("up", lambda: B.qlinear_w8a8(self.h1, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)),
+            ("down", lambda: B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
+                                            steer_dir=self.steer_dir, steer_alpha=self.steer_alpha,
+                                            stream=stream)),
+        ]
+
     def stages(self, h, stream=None):
         """Yields after each stage (for per-stage timing or checks)."""
-        p = self.packed
-        B.qlinear_w8a8(h, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)
-        yield "qkv"
-        copy_columns(self.a, self.qkv, 2 * self.width, self.width, stream)
-        yield "attention"
-        B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)
-        yield "out"
-        B.qlinear_w8a8(self.h1, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)
-        yield "up"
-        B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
-                       steer_dir=self.steer_dir, steer_alpha=self.steer_alpha, stream=stream)
-        yield "down"
+        for name, fn in self.calls(h, stream):
+            fn()
+            yield name
 
     def run(self, h, stream=None):
         for _ in self.stages(h, stream):
@@ -100,23 +106,25 @@ class DitBlockFullW8A8:
         need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, 1) for k in (width, mlp))
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-    def stages(self, h, stream=None):
+    def calls(self, h, stream=None):
+        """The stages as (name, callable) pairs, in order (see DitBlockW8A8.calls)."""
         p = self.packed
-        B.layernorm(h, *self.ln1, eps=self.eps, y=self.n1, stream=stream)
-        yield "ln1"
-        B.qlinear_w8a8(self.n1, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)
-        yield "qkv"
-        B.attention(self.qkv, self.heads, self.seq, out=self.a, stream=stream)
-        yield "attention"
-        B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)
-        yield "out"
-        B.layernorm(self.h1, *self.ln2, eps=self.eps, y=self.n2, stream=stream)
-        yield "ln2"
-        B.qlinear_w8a8(self.n2, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)
-        yield "up"
-        B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
-                       steer_dir=self.steer_dir, steer_alpha=self.steer_alpha, stream=stream)
-        yield "down"
+        return [
+            ("ln1", lambda: B.layernorm(h, *self.ln1, eps=self.eps, y=self.n1, stream=stream)),
+            ("qkv", lambda: B.qlinear_w8a8(self.n1, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)),
+            ("attention", lambda: B.attention(self.qkv, self.heads, self.seq, out=self.a, stream=stream)),
+            ("out", lambda: B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)),
+            ("ln2", lambda: B.layernorm(self.h1, *self.ln2, eps=self.eps, y=self.n2, stream=stream)),
+            ("up", lambda: B.qlinear_w8a8(self.n2, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)),
+            ("down", lambda: B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
+                                            steer_dir=self.steer_dir, steer_alpha=self.steer_alpha,
+                                            stream=stream)),
+        ]
+
+    def stages(self, h, stream=None):
+        for name, fn in self.calls(h, stream):
+            fn()
+            yield name
 
     def run(self, h, stream=None):
         for _ in self.stages(h, stream):
