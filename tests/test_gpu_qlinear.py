@@ -243,14 +243,17 @@ TILES = ["256x256x4x2", "256x192x4x2", "256x128x4x2", "128x256x2x4", "128x192x2x
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("mode", ["w8a8", "w8a16", "w4a16"])
-@pytest.mark.parametrize("N", [460, 520])
-def test_every_tile_variant(q, tile, mode, N, monkeypatch):
+@pytest.mark.parametrize("N,K", [(460, 352), (520, 352), (520, 416), (460, 32)])
+def test_every_tile_variant(q, tile, mode, N, K, monkeypatch):
     """Every macro-tile variant of the tiled kernel (forced through the tuning
     override) on ragged shapes that span several tiles and a K tail; N = 460
     takes the element-wise epilogue (N % 8 != 0), N = 520 the vector one with
-    a partial last tile."""
+    a partial last tile.  K = 352 and 416 give an odd and an even number of
+    K-steps in each mode (128 int8 k or 64 fp16 k per step: the 4-wave tiles
+    alternate two register sets, so both parities and the one-step case,
+    K = 32, are covered)."""
     monkeypatch.setenv("ARIA_QLINEAR_TILE", tile)
-    M, K = 300, 352
+    M = 300
     log(f"{mode} tile {tile} {M}x{K}x{N}")
     x, w = _rand(M, K, N, 4242)
     e = _epi_inputs(M, N, 9, bias=True, gelu=True, residual=True, steer=True)

@@ -97,3 +97,24 @@ def test_w16a16_full_width_m2048(q):
     log("w16a16 2048x1536x6144")
     out, ref = run(q, lin.x, lin.w, {"bias": lin.bias, "gelu": True}, rows)
     assert_close(out, ref, "w16a16 2048x1536x6144")
+
+
+TILES = ["256x256x4x2", "256x192x4x2", "256x128x4x2", "128x256x2x4", "128x192x2x2", "128x128x2x2",
+         "64x192x2x2", "128x64x2x2", "64x128x2x2", "64x64x2x2"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("N,K", [(460, 352), (520, 416), (460, 32)])
+def test_w16a16_every_tile_variant(q, tile, N, K, monkeypatch):
+    """Every macro-tile variant in fp16 mode (forced through the tuning
+    override), with an even (K = 352: 6 K-steps of 64) and an odd (K = 416: 7)
+    number of K-steps, the one-step case (K = 32), and both epilogue forms."""
+    rng = np.random.default_rng(N + K)
+    monkeypatch.setenv("ARIA_QLINEAR_TILE", tile)
+    M = 300
+    log(f"w16a16 tile {tile} {M}x{K}x{N}")
+    x, w = _case(M, K, N, 4300 + N + K)
+    e = {"bias": (rng.standard_normal(N) * 0.1).astype(np.float16), "gelu": True,
+         "residual": rng.standard_normal((M, N)).astype(np.float16)}
+    out, ref = run(q, x, w, e)
+    assert_close(out, ref, f"w16a16 {tile} {M}x{K}x{N}")
