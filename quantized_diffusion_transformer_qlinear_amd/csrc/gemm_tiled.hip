@@ -10,8 +10,8 @@
 //   W16A16: acc = sum_k X[m][k] * Wt[n][k]  (fp32);  y = acc
 // then y -> + bias -> GELU -> + residual -> + alpha d -> fp16.
 //
-// Design (gfx950): a workgroup of WM x WN waves owns a BM x BN output tile;
-// each wave owns (BM/WM) x (BN/WN) as 32x32 blocks on the matrix cores
+// Design (gfx950): a workgroup of WM x WN waves (4, 8 or 12) owns a BM x BN
+// output tile; each wave owns (BM/WM) x (BN/WN) as 32x32 blocks on the matrix cores
 // (v_mfma_i32_32x32x32_i8 or v_mfma_f32_32x32x16_f16).  Both operands live in
 // LDS as rows of 128 bytes (128 int8 k or 64 fp16 k) plus a 16-byte pad that
 // spreads the 32 rows of an operand fragment over all banks; a K-step is 4
@@ -75,9 +75,9 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int NA = BM * 8;                   // 16-byte A chunks per K-step
     constexpr int NB = BN * T::BCH;              // 16-byte packed B chunks per K-step
-    constexpr int LA = NA / NT;
+    constexpr int LA = (NA + NT - 1) / NT;
     constexpr int LB = (NB + NT - 1) / NT;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && NA % NT == 0, "tile shape");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && NA % WAVE == 0 && NB % WAVE == 0, "tile shape");
 
     __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
 
@@ -116,10 +116,8 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
         const uint32_t off = (uint32_t)(m0 + row) * (uint32_t)K * T::AEB + (uint32_t)k * T::AEB;
         RA[set][i] = buf_load16(ra, k < K && m0 + row < M ? off : OOB);
     };
-    // threads past the last B chunk (NB not a multiple of 256) redo chunk c % NB:
-    // the same bytes land at the same LDS address, which keeps the loop branch-free
     auto load_b = [&](int kt, int i, int set) {
-        const int c = (tid + i * NT) % NB, row = c / T::BCH, ch = c % T::BCH;
+        const int c = tid + i * NT, row = c / T::BCH, ch = c % T::BCH;
         const int k = kt * T::KSTEP + ch * T::KPB;
         const bool in = k < K && n0 + row < N;
         const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : MODE == 3 ? 2 * k : k);
@@ -131,7 +129,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
         *reinterpret_cast<v4i*>(&lds[buf][row * ROWB + ch * 16]) = RA[set][i];
     };
     auto store_b = [&](int buf, int i, int set) {
-        const int c = (tid + i * NT) % NB;
+        const int c = tid + i * NT;
         const int row = c / T::BCH, ch = c % T::BCH;
         char* dst = &lds[buf][(BM + row) * ROWB + ch * (T::KPB * 2 / (MODE == 0 ? 2 : 1))];
         if constexpr (MODE == 0 || MODE == 3) {
@@ -148,17 +146,27 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
             for (int q = 0; q < 4; q++) reinterpret_cast<v4i*>(dst)[q] = o[q];
         }
     };
+    // chunk i of this thread exists unless the chunk count is not a multiple
+    // of the thread count and the thread is past the end: a whole wave at a
+    // time (both counts are multiples of 64), so the test is wave-uniform
+    const int wbase = __builtin_amdgcn_readfirstlane(wave) * WAVE;
+    auto has_a = [&](int i) { return NA % NT == 0 || wbase + i * NT < NA; };
+    auto has_b = [&](int i) { return NB % NT == 0 || wbase + i * NT < NB; };
     auto load_part = [&](int kt, int p, int set) {
 #pragma unroll
-        for (int i = p; i < LA; i += 4) load_a(kt, i, set);
+        for (int i = p; i < LA; i += 4)
+            if (has_a(i)) load_a(kt, i, set);
 #pragma unroll
-        for (int i = p; i < LB; i += 4) load_b(kt, i, set);
+        for (int i = p; i < LB; i += 4)
+            if (has_b(i)) load_b(kt, i, set);
     };
     auto store_part = [&](int buf, int p, int set) {
 #pragma unroll
-        for (int i = p; i < LA; i += 4) store_a(buf, i, set);
+        for (int i = p; i < LA; i += 4)
+            if (has_a(i)) store_a(buf, i, set);
 #pragma unroll
-        for (int i = p; i < LB; i += 4) store_b(buf, i, set);
+        for (int i = p; i < LB; i += 4)
+            if (has_b(i)) store_b(buf, i, set);
     };
 
     typename T::acc_t acc[FM][FN];
@@ -380,19 +388,22 @@ struct TileCfg {
 // mode W8A8 / W8A16 / W4A16 / W16A16: for each tile, waves x BM x BN x K / time
 // (relative units), the median over eight layer shapes at M = 2048 (the DiT
 // block's four linears at width 1536 and the four of the 1.2B-scale step at
-// width 2048), with two W8A16 / W16A16 entries of 128x128 nudged so that the
-// picker's choice is within 1 % of the fastest tile on those shapes.  The
-// picker minimises
+// width 2048), then adjusted so that the picker's choice is within 1 % of the
+// fastest tile on those shapes.  The picker minimises
 //   ceil(tiles / CUs) * BM * BN / eff
-// i.e. it trades CU fill (whole waves of tiles) against per-tile efficiency;
-// 8-wave workgroups put two waves on every SIMD so one can issue while the
-// other waits on LDS or memory.
+// i.e. it trades CU fill (whole waves of tiles) against per-tile efficiency.
+// 8- and 12-wave workgroups put two or three waves on every SIMD so one can
+// issue while the others wait on LDS or memory; the 12-wave 256x192 tile (64x64
+// per wave) is the fastest for W8A8, W8A16 and W16A16 at N = 4608 or 6144, but
+// not for W4A16, whose 384 packed-weight chunks per K-step load and decode on
+// only half of its waves.
 constexpr TileCfg kTiles[] = {
-    {256, 256, 4, 2, {4044.f, 2467.f, 2409.f, 2635.f}}, {256, 192, 4, 2, {3838.f, 2229.f, 2125.f, 2375.f}},
-    {256, 128, 4, 2, {3225.f, 2040.f, 1670.f, 1994.f}}, {128, 256, 2, 4, {3421.f, 1991.f, 1797.f, 2055.f}},
-    {128, 192, 2, 2, {2419.f, 1556.f, 1328.f, 1671.f}}, {128, 128, 2, 2, {2764.f, 1899.f, 1444.f, 1844.f}},
-    {64, 192, 2, 2, {2333.f, 1383.f, 1007.f, 1358.f}},  {128, 64, 2, 2, {2370.f, 1318.f, 1074.f, 1358.f}},
-    {64, 128, 2, 2, {2361.f, 1323.f, 1138.f, 1355.f}},  {64, 64, 2, 2, {2167.f, 1163.f, 828.f, 1156.f}}};
+    {256, 192, 4, 3, {3942.f, 2476.f, 1682.f, 2472.f}}, {256, 256, 4, 2, {3948.f, 2469.f, 2599.f, 2686.f}},
+    {256, 192, 4, 2, {3727.f, 2242.f, 2218.f, 2348.f}}, {256, 128, 4, 2, {3202.f, 1977.f, 1859.f, 2068.f}},
+    {128, 256, 2, 4, {3357.f, 1961.f, 1777.f, 2106.f}}, {128, 192, 2, 2, {2399.f, 1525.f, 1255.f, 1644.f}},
+    {128, 128, 2, 2, {2696.f, 1886.f, 1434.f, 1895.f}}, {64, 192, 2, 2, {2347.f, 1377.f, 1037.f, 1406.f}},
+    {128, 64, 2, 2, {2245.f, 1333.f, 1185.f, 1352.f}},  {64, 128, 2, 2, {2304.f, 1291.f, 1116.f, 1344.f}},
+    {64, 64, 2, 2, {2095.f, 1181.f, 950.f, 1149.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -440,7 +451,7 @@ hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const 
 #define ARIA_TILE(BM_, BN_, WM_, WN_)                          \
     if (t.bm == BM_ && t.bn == BN_ && t.wm == WM_ && t.wn == WN_) \
         return launch_one<MODE, BM_, BN_, WM_, WN_>(a, b, s, sa, y, M, N, K, e, st);
-    ARIA_TILE(256, 256, 4, 2) ARIA_TILE(256, 192, 4, 2) ARIA_TILE(256, 128, 4, 2) ARIA_TILE(128, 256, 2, 4)
+    ARIA_TILE(256, 192, 4, 3) ARIA_TILE(256, 256, 4, 2) ARIA_TILE(256, 192, 4, 2) ARIA_TILE(256, 128, 4, 2) ARIA_TILE(128, 256, 2, 4)
     ARIA_TILE(128, 192, 2, 2) ARIA_TILE(128, 128, 2, 2) ARIA_TILE(64, 192, 2, 2) ARIA_TILE(128, 64, 2, 2)
     ARIA_TILE(64, 128, 2, 2) ARIA_TILE(64, 64, 2, 2)
 #undef ARIA_TILE
