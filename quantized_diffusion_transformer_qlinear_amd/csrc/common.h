@@ -66,6 +66,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ v2u buf_load8(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ half_t buf_load_h(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
 }

@@ -27,13 +27,14 @@ __device__ __forceinline__ void dec8(v4i w, v4i& lo, v4i& hi) {
     hi = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
 }
 
-// 32 nibbles (4 dwords; even k in the low nibble) -> 32 fp16 values fp16(q * s):
-// (n ^ 8) = q + 8 -> fp16(0x6400 | u) - 1032 = q (exact) -> times s (one rounding).
-// `sc` holds the group scale in both halves.
-__device__ __forceinline__ void dec4(v4i w, v2h sc, v4i out[4]) {
+// 8 ND nibbles (ND dwords; even k in the low nibble) -> 8 ND fp16 values
+// fp16(q * s): (n ^ 8) = q + 8 -> fp16(0x6400 | u) - 1032 = q (exact) -> times s
+// (one rounding).  `sc` holds the group scale in both halves.
+template <int ND = 4>
+__device__ __forceinline__ void dec4(v4i w, v2h sc, v4i out[ND]) {
     const v2h bias = {(half_t)1032.0f, (half_t)1032.0f};
 #pragma unroll
-    for (int d = 0; d < 4; d++) {
+    for (int d = 0; d < ND; d++) {
         const u32 u = (u32)w[d] ^ 0x88888888u;
         const u32 t0 = u & 0x0F0F0F0Fu;          // bytes: k0 k2 k4 k6
         const u32 t1 = (u >> 4) & 0x0F0F0F0Fu;   // bytes: k1 k3 k5 k7
@@ -49,7 +50,8 @@ __device__ __forceinline__ void dec4(v4i w, v2h sc, v4i out[4]) {
         out[d] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     }
 }
-__device__ __forceinline__ void dec4(v4i w, half_t s, v4i out[4]) { dec4(w, v2h{s, s}, out); }
+template <int ND = 4>
+__device__ __forceinline__ void dec4(v4i w, half_t s, v4i out[ND]) { dec4<ND>(w, v2h{s, s}, out); }
 // ... with the scale given as its 16 bits in the low half of a dword (as a
 // 16-bit buffer load returns it): kept in a dword, a scale array stays in
 // registers.

@@ -73,8 +73,14 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     constexpr int ROWB = 144;                    // LDS bytes per row (128 + pad)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
+    // 4-bit weights come in 8-byte chunks (16 k) where 16-byte ones would leave
+    // waves idle: the 12-wave 256x192 tile has 384 of those for 768 threads
+    constexpr bool HALF4 = MODE == 2 && (BN * T::BCH) % (WM * WN * WAVE) != 0 &&
+                           (2 * BN * T::BCH) % (WM * WN * WAVE) == 0;
+    constexpr int KPB = HALF4 ? T::KPB / 2 : T::KPB;   // k per packed B chunk
+    constexpr int BCH = HALF4 ? 2 * T::BCH : T::BCH;   // packed B chunks per row per K-step
     constexpr int NA = BM * 8;                   // 16-byte A chunks per K-step
-    constexpr int NB = BN * T::BCH;              // 16-byte packed B chunks per K-step
+    constexpr int NB = BN * BCH;                 // packed B chunks per K-step
     constexpr int LA = (NA + NT - 1) / NT;
     constexpr int LB = (NB + NT - 1) / NT;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && NA % WAVE == 0 && NB % WAVE == 0, "tile shape");
@@ -117,11 +123,16 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
         RA[set][i] = buf_load16(ra, k < K && m0 + row < M ? off : OOB);
     };
     auto load_b = [&](int kt, int i, int set) {
-        const int c = tid + i * NT, row = c / T::BCH, ch = c % T::BCH;
-        const int k = kt * T::KSTEP + ch * T::KPB;
+        const int c = tid + i * NT, row = c / BCH, ch = c % BCH;
+        const int k = kt * T::KSTEP + ch * KPB;
         const bool in = k < K && n0 + row < N;
         const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : MODE == 3 ? 2 * k : k);
-        RB[set][i] = buf_load16(rb, in ? off : OOB);
+        if constexpr (HALF4) {
+            const v2u h = buf_load8(rb, in ? off : OOB);
+            RB[set][i] = v4i{(int)h[0], (int)h[1], 0, 0};
+        } else {
+            RB[set][i] = buf_load16(rb, in ? off : OOB);
+        }
         if (MODE == 2) RS[set][i] = S[(int64_t)min(n0 + row, N - 1) * G + min(k, K - 32) / 32];
     };
     auto store_a = [&](int buf, int i, int set) {
@@ -130,8 +141,8 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     };
     auto store_b = [&](int buf, int i, int set) {
         const int c = tid + i * NT;
-        const int row = c / T::BCH, ch = c % T::BCH;
-        char* dst = &lds[buf][(BM + row) * ROWB + ch * (T::KPB * 2 / (MODE == 0 ? 2 : 1))];
+        const int row = c / BCH, ch = c % BCH;
+        char* dst = &lds[buf][(BM + row) * ROWB + ch * (KPB * 2 / (MODE == 0 ? 2 : 1))];
         if constexpr (MODE == 0 || MODE == 3) {
             *reinterpret_cast<v4i*>(dst) = RB[set][i];
         } else if constexpr (MODE == 1) {
@@ -140,10 +151,11 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
             reinterpret_cast<v4i*>(dst)[0] = lo;
             reinterpret_cast<v4i*>(dst)[1] = hi;
         } else {
-            v4i o[4];
-            dec4(RB[set][i], RS[set][i], o);
+            constexpr int ND = HALF4 ? 2 : 4;
+            v4i o[ND];
+            dec4<ND>(RB[set][i], RS[set][i], o);
 #pragma unroll
-            for (int q = 0; q < 4; q++) reinterpret_cast<v4i*>(dst)[q] = o[q];
+            for (int q = 0; q < ND; q++) reinterpret_cast<v4i*>(dst)[q] = o[q];
         }
     };
     // chunk i of this thread exists unless the chunk count is not a multiple
@@ -394,16 +406,14 @@ struct TileCfg {
 // i.e. it trades CU fill (whole waves of tiles) against per-tile efficiency.
 // 8- and 12-wave workgroups put two or three waves on every SIMD so one can
 // issue while the others wait on LDS or memory; the 12-wave 256x192 tile (64x64
-// per wave) is the fastest for W8A8, W8A16 and W16A16 at N = 4608 or 6144, but
-// not for W4A16, whose 384 packed-weight chunks per K-step load and decode on
-// only half of its waves.
+// per wave) is the fastest in every mode at N = 4608 or 6144.
 constexpr TileCfg kTiles[] = {
-    {256, 192, 4, 3, {3942.f, 2476.f, 1682.f, 2472.f}}, {256, 256, 4, 2, {3948.f, 2469.f, 2599.f, 2686.f}},
-    {256, 192, 4, 2, {3727.f, 2242.f, 2218.f, 2348.f}}, {256, 128, 4, 2, {3202.f, 1977.f, 1859.f, 2068.f}},
-    {128, 256, 2, 4, {3357.f, 1961.f, 1777.f, 2106.f}}, {128, 192, 2, 2, {2399.f, 1525.f, 1255.f, 1644.f}},
-    {128, 128, 2, 2, {2696.f, 1886.f, 1434.f, 1895.f}}, {64, 192, 2, 2, {2347.f, 1377.f, 1037.f, 1406.f}},
-    {128, 64, 2, 2, {2245.f, 1333.f, 1185.f, 1352.f}},  {64, 128, 2, 2, {2304.f, 1291.f, 1116.f, 1344.f}},
-    {64, 64, 2, 2, {2095.f, 1181.f, 950.f, 1149.f}}};
+    {256, 192, 4, 3, {3942.f, 2476.f, 2470.f, 2472.f}}, {256, 256, 4, 2, {3948.f, 2469.f, 2562.f, 2686.f}},
+    {256, 192, 4, 2, {3727.f, 2242.f, 2217.f, 2348.f}}, {256, 128, 4, 2, {3202.f, 1977.f, 1982.f, 2068.f}},
+    {128, 256, 2, 4, {3357.f, 1961.f, 1793.f, 2106.f}}, {128, 192, 2, 2, {2399.f, 1525.f, 1492.f, 1644.f}},
+    {128, 128, 2, 2, {2696.f, 1886.f, 1576.f, 1895.f}}, {64, 192, 2, 2, {2347.f, 1377.f, 1138.f, 1406.f}},
+    {128, 64, 2, 2, {2245.f, 1333.f, 1222.f, 1352.f}},  {64, 128, 2, 2, {2304.f, 1291.f, 1104.f, 1344.f}},
+    {64, 64, 2, 2, {2095.f, 1181.f, 959.f, 1149.f}}};
 
 int num_cus() {
     static int cus = 0;
