@@ -237,7 +237,7 @@ def test_w8a8_mlp_up_full_size(q):
     assert_close(out, ref, "w8a8 2048x1536x6144")
 
 
-TILES = ["256x192x4x3", "256x256x4x2", "256x192x4x2", "256x128x4x2", "128x256x2x4", "128x192x2x2", "128x128x2x2",
+TILES = ["256x192x4x3", "256x256x4x4", "256x192x4x2", "256x128x4x2", "128x256x2x4", "128x192x2x2", "128x128x2x2",
          "64x192x2x2", "128x64x2x2", "64x128x2x2", "64x64x2x2"]
 
 
