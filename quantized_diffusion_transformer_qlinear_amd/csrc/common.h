@@ -78,8 +78,10 @@ __device__ __forceinline__ half_t buf_load_h(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t off, char* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
 }
-__device__ __forceinline__ void buf_store8(v2u v, rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+// 8-byte store with the non-temporal cache policy (aux bit 1 = nt on gfx950):
+// for outputs that the writing kernel never reads back.
+__device__ __forceinline__ void buf_store8_nt(v2u v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 2);
 }
 
 // XCD-aware remap of a linear workgroup id: the hardware deals workgroups

