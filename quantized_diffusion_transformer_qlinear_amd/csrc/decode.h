@@ -1,8 +1,9 @@
 // Register decoders for packed weights (shared by the tiled and skinny GEMMs).
-// Both build the fp16 bit pattern 0x6400 | u, whose value is 1024 + u for an
-// integer u in [0, 1023], and subtract the bias with packed-half arithmetic:
-// exact for the integer, then (4-bit) one multiply by the group scale, which
-// rounds once to fp16.
+// Both build fp16 bit patterns whose value is a fixed offset plus the unsigned
+// code u (0x6400 | u = 1024 + u; for 4-bit codes also 0x5400 | u << 4 =
+// 64 + u) and subtract the offset with packed-half arithmetic: exact for the
+// integer, then (4-bit) one multiply by the group scale, which rounds once to
+// fp16.
 #pragma once
 
 #include "common.h"
@@ -28,22 +29,26 @@ __device__ __forceinline__ void dec8(v4i w, v4i& lo, v4i& hi) {
 }
 
 // 8 ND nibbles (ND dwords; even k in the low nibble) -> 8 ND fp16 values
-// fp16(q * s): (n ^ 8) = q + 8 -> fp16(0x6400 | u) - 1032 = q (exact) -> times s
-// (one rounding).  `sc` holds the group scale in both halves.
+// fp16(q * s).  For the pair k = 2j, 2j+1 (byte j of a dword) a byte permute
+// copies byte j into bytes 0 and 2; one three-input bit operation then keeps
+// the low nibble in the low half and the high nibble at bits 4-7 of the high
+// half, flips each nibble's top bit ((n ^ 8) = q + 8 = u) and sets the two
+// exponents, so the low half reads 1024 + u (0x6400 | u: unit steps) and the
+// high half 64 + u (0x5400 | u << 4: exponent 6, where mantissa bit 4 is
+// worth 1).  One packed subtract of (1032, 72) leaves q exactly, one packed
+// multiply by the group scale rounds once.  Four VALU ops per pair.
 template <int ND = 4>
 __device__ __forceinline__ void dec4(v4i w, v2h sc, v4i out[ND]) {
-    const v2h bias = {(half_t)1032.0f, (half_t)1032.0f};
+    const v2h bias = {(half_t)1032.0f, (half_t)72.0f};
 #pragma unroll
     for (int d = 0; d < ND; d++) {
-        const u32 u = (u32)w[d] ^ 0x88888888u;
-        const u32 t0 = u & 0x0F0F0F0Fu;          // bytes: k0 k2 k4 k6
-        const u32 t1 = (u >> 4) & 0x0F0F0F0Fu;   // bytes: k1 k3 k5 k7
+        const u32 u = (u32)w[d];
         u32 o[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            // k = 2j (byte j of t0) in the low half, k = 2j+1 (byte j of t1) in the high half
-            const u32 sel = 0x0C000C00u | (u32)j | ((u32)(4 + j) << 16);
-            const u32 p = __builtin_amdgcn_perm(t1, t0, sel) | 0x64006400u;
+            // selector bytes j, 0x0C (zero), j, 0x0C: the dword reads b_j, 0, b_j, 0
+            const u32 b = __builtin_amdgcn_perm(0u, u, 0x0C000C00u | (u32)j | ((u32)j << 16));
+            const u32 p = (b & 0x00F0000Fu) ^ 0x54806408u;
             v2h h = (__builtin_bit_cast(v2h, p) - bias) * sc;
             o[j] = __builtin_bit_cast(u32, h);
         }
