@@ -113,19 +113,35 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     // tiles lack the registers for it and hide latency with their second wave
     // per SIMD instead
     constexpr int NSET = WM * WN == 4 ? 2 : 1;
+    // PIN: every part's loads and stores stay in their sub-step (a scheduling
+    // barrier after each), and every wave issues the same loads (see load_a),
+    // so the compiler's waits give each load a whole K-step to land; without
+    // it the compiler gathered the stores of several parts into one sub-step
+    // and, around the branches of chunks that some waves skip, waited for all
+    // loads.  Measured per tile and mode over eight layer shapes: +5-9 % for
+    // 8-wave tiles and for W8A8 on the 12-wave tile, +2 % W8A16 there; the
+    // W4A16 12-wave tile and the 16-wave tile outside W8A8 lose 3-5 % with it,
+    // so they keep the free schedule.  The 4-wave tiles (two register sets)
+    // always pin.
+    constexpr bool PIN = NSET == 2 || WM * WN == 8 || MODE == 0 || (WM * WN == 12 && MODE != 2);
     v4i RA[NSET][LA], RB[NSET][LB > 0 ? LB : 1];
     half_t RS[NSET][LB > 0 ? LB : 1];
 
-    auto load_a = [&](int kt, int i, int set) {
+    // `ok` false: the chunk does not exist for this wave.  With PIN the load
+    // still issues (an out-of-range offset reads zero and moves no data), so
+    // every wave issues the same loads in the same order and the compiler can
+    // count them exactly when it places its waits (a branch around a load
+    // makes it wait for the loads of both paths); otherwise it is skipped.
+    auto load_a = [&](int kt, int i, int set, bool ok) {
         const int c = tid + i * NT, row = c / 8, ch = c % 8;
         const int k = kt * T::KSTEP + ch * (16 / T::AEB);
         const uint32_t off = (uint32_t)(m0 + row) * (uint32_t)K * T::AEB + (uint32_t)k * T::AEB;
-        RA[set][i] = buf_load16(ra, k < K && m0 + row < M ? off : OOB);
+        RA[set][i] = buf_load16(ra, ok && k < K && m0 + row < M ? off : OOB);
     };
-    auto load_b = [&](int kt, int i, int set) {
+    auto load_b = [&](int kt, int i, int set, bool ok) {
         const int c = tid + i * NT, row = c / BCH, ch = c % BCH;
         const int k = kt * T::KSTEP + ch * KPB;
-        const bool in = k < K && n0 + row < N;
+        const bool in = ok && k < K && n0 + row < N;
         const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : MODE == 3 ? 2 * k : k);
         if constexpr (HALF4) {
             const v2u h = buf_load8(rb, in ? off : OOB);
@@ -162,15 +178,17 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     // of the thread count and the thread is past the end: a whole wave at a
     // time (both counts are multiples of 64), so the test is wave-uniform
     const int wbase = __builtin_amdgcn_readfirstlane(wave) * WAVE;
-    auto has_a = [&](int i) { return NA % NT == 0 || wbase + i * NT < NA; };
-    auto has_b = [&](int i) { return NB % NT == 0 || wbase + i * NT < NB; };
+    // (rounds that every wave fills are folded to true only under PIN: on the
+    // free schedule the branches happen to place the code better, by 1-3 %)
+    auto has_a = [&](int i) { return (PIN && (i + 1) * NT <= NA) || NA % NT == 0 || wbase + i * NT < NA; };
+    auto has_b = [&](int i) { return (PIN && (i + 1) * NT <= NB) || NB % NT == 0 || wbase + i * NT < NB; };
     auto load_part = [&](int kt, int p, int set) {
 #pragma unroll
         for (int i = p; i < LA; i += 4)
-            if (has_a(i)) load_a(kt, i, set);
+            if (PIN || has_a(i)) load_a(kt, i, set, has_a(i));
 #pragma unroll
         for (int i = p; i < LB; i += 4)
-            if (has_b(i)) load_b(kt, i, set);
+            if (PIN || has_b(i)) load_b(kt, i, set, has_b(i));
     };
     auto store_part = [&](int buf, int p, int set) {
 #pragma unroll
@@ -244,7 +262,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
                     __syncthreads();
                 }
             }
-            if constexpr (NSET == 2) __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
         }
     };
     read_frags(lds[0], 0, 0);
@@ -412,14 +430,15 @@ struct TileCfg {
 // 12-wave 256x192 and 16-wave 256x256 tiles) beat 64x96 and 64x128 per wave
 // with fewer waves (the 16-wave 256x256 entries are the 8-wave 256x256 ones
 // scaled by what the two measured against each other: +17 % W8A8, +7 %
-// W8A16, +2 % W16A16, equal for W4A16).
+// W8A16, +2 % W16A16, equal for W4A16).  Every entry was then scaled by the
+// measured gain of the pinned schedule (geomean over the same shapes).
 constexpr TileCfg kTiles[] = {
-    {256, 192, 4, 3, {3942.f, 2476.f, 2470.f, 2472.f}}, {256, 256, 4, 4, {4620.f, 2640.f, 2562.f, 2740.f}},
-    {256, 192, 4, 2, {3727.f, 2242.f, 2217.f, 2348.f}}, {256, 128, 4, 2, {3202.f, 1977.f, 1982.f, 2068.f}},
-    {128, 256, 2, 4, {3357.f, 1961.f, 1793.f, 2106.f}}, {128, 192, 2, 2, {2399.f, 1525.f, 1492.f, 1644.f}},
-    {128, 128, 2, 2, {2696.f, 1886.f, 1576.f, 1895.f}}, {64, 192, 2, 2, {2347.f, 1377.f, 1138.f, 1406.f}},
-    {128, 64, 2, 2, {2245.f, 1333.f, 1222.f, 1352.f}},  {64, 128, 2, 2, {2304.f, 1291.f, 1104.f, 1344.f}},
-    {64, 64, 2, 2, {2095.f, 1181.f, 959.f, 1149.f}}};
+    {256, 192, 4, 3, {4304.f, 2521.f, 2432.f, 2504.f}}, {256, 256, 4, 4, {4701.f, 2640.f, 2560.f, 2736.f}},
+    {256, 192, 4, 2, {3927.f, 2397.f, 2187.f, 2483.f}}, {256, 128, 4, 2, {3344.f, 2122.f, 2008.f, 2130.f}},
+    {128, 256, 2, 4, {3470.f, 2126.f, 1833.f, 2127.f}}, {128, 192, 2, 2, {2388.f, 1528.f, 1496.f, 1643.f}},
+    {128, 128, 2, 2, {2683.f, 1889.f, 1577.f, 1894.f}}, {64, 192, 2, 2, {2335.f, 1379.f, 1140.f, 1406.f}},
+    {128, 64, 2, 2, {2235.f, 1335.f, 1222.f, 1353.f}},  {64, 128, 2, 2, {2292.f, 1290.f, 1105.f, 1340.f}},
+    {64, 64, 2, 2, {2076.f, 1182.f, 960.f, 1153.f}}};
 
 int num_cus() {
     static int cus = 0;
