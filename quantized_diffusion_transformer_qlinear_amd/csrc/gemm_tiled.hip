@@ -10,7 +10,8 @@
 //   W16A16: acc = sum_k X[m][k] * Wt[n][k]  (fp32);  y = acc
 // then y -> + bias -> GELU -> + residual -> + alpha d -> fp16.
 //
-// Design (gfx950): a workgroup of WM x WN waves (4, 8, 12 or 16) owns a BM x BN
+// Design (gfx950): a workgroup of WM x WN waves (4, 8, 12 or 16; a 4-wave tile
+// may also run as two such groups that split the K-steps) owns a BM x BN
 // output tile; each wave owns (BM/WM) x (BN/WN) as 32x32 blocks on the matrix cores
 // (v_mfma_i32_32x32x32_i8 or v_mfma_f32_32x32x16_f16).  Both operands live in
 // LDS as rows of 128 bytes (128 int8 k or 64 fp16 k) plus a 16-byte pad that
@@ -64,8 +65,8 @@ struct ModeT<3> {  // W16A16 (fp16 weights, the unquantized rung)
 
 }  // namespace
 
-template <int MODE, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* __restrict__ Aptr, const uint8_t* __restrict__ Bq,
+template <int MODE, int BM, int BN, int WM, int WN, int KS>
+__global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const void* __restrict__ Aptr, const uint8_t* __restrict__ Bq,
                                                          const half_t* __restrict__ S, const half_t* __restrict__ sa,
                                                          half_t* Y, int M, int N, int K, Epi epi) {
     using T = ModeT<MODE>;
@@ -85,7 +86,12 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     constexpr int LB = (NB + NT - 1) / NT;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && NA % WAVE == 0 && NB % WAVE == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
+    // KS = 2: two groups of WM x WN waves share the tile and split its
+    // K-steps (group g takes g, g + 2, ...), each with its own double buffer
+    // and pipeline; their partial sums meet in LDS before the epilogue.  For
+    // tiles that leave one workgroup per CU this doubles the waves per SIMD.
+    static_assert(KS == 1 || KS == 2, "K split");
+    __shared__ __attribute__((aligned(16))) char lds[2 * KS][(BM + BN) * ROWB];
 
     // Tile order: groups of GM row-blocks, column-major inside a group, after
     // the XCD remap; the 32 consecutive tiles one XCD runs then form a compact
@@ -98,8 +104,11 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     const int in_group = bid % (GM * ntn);
     const int tm = first_m + in_group % gsize, tn = in_group / gsize;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    // tid and wave count within the thread's K group
+    const int grp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT);
+    const int tid = (int)threadIdx.x % NT, wave = tid / WAVE, lane = tid % WAVE;
     const int wm = wave / WN, wn = wave % WN;
+    char(*const glds)[(BM + BN) * ROWB] = lds + 2 * grp;   // this group's two buffers
 
     const uint32_t abytes = (uint32_t)M * (uint32_t)K * T::AEB;
     const uint32_t browb = MODE == 2 ? (uint32_t)K / 2 : MODE == 3 ? (uint32_t)K * 2 : (uint32_t)K;
@@ -134,13 +143,13 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     // makes it wait for the loads of both paths); otherwise it is skipped.
     auto load_a = [&](int kt, int i, int set, bool ok) {
         const int c = tid + i * NT, row = c / 8, ch = c % 8;
-        const int k = kt * T::KSTEP + ch * (16 / T::AEB);
+        const int k = (kt * KS + grp) * T::KSTEP + ch * (16 / T::AEB);
         const uint32_t off = (uint32_t)(m0 + row) * (uint32_t)K * T::AEB + (uint32_t)k * T::AEB;
         RA[set][i] = buf_load16(ra, ok && k < K && m0 + row < M ? off : OOB);
     };
     auto load_b = [&](int kt, int i, int set, bool ok) {
         const int c = tid + i * NT, row = c / BCH, ch = c % BCH;
-        const int k = kt * T::KSTEP + ch * KPB;
+        const int k = (kt * KS + grp) * T::KSTEP + ch * KPB;
         const bool in = ok && k < K && n0 + row < N;
         const uint32_t off = (uint32_t)(n0 + row) * browb + (uint32_t)(MODE == 2 ? k / 2 : MODE == 3 ? 2 * k : k);
         if constexpr (HALF4) {
@@ -153,12 +162,12 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     };
     auto store_a = [&](int buf, int i, int set) {
         const int c = tid + i * NT, row = c / 8, ch = c % 8;
-        *reinterpret_cast<v4i*>(&lds[buf][row * ROWB + ch * 16]) = RA[set][i];
+        *reinterpret_cast<v4i*>(&glds[buf][row * ROWB + ch * 16]) = RA[set][i];
     };
     auto store_b = [&](int buf, int i, int set) {
         const int c = tid + i * NT;
         const int row = c / BCH, ch = c % BCH;
-        char* dst = &lds[buf][(BM + row) * ROWB + ch * (KPB * 2 / (MODE == 0 ? 2 : 1))];
+        char* dst = &glds[buf][(BM + row) * ROWB + ch * (KPB * 2 / (MODE == 0 ? 2 : 1))];
         if constexpr (MODE == 0 || MODE == 3) {
             *reinterpret_cast<v4i*>(dst) = RB[set][i];
         } else if constexpr (MODE == 1) {
@@ -205,7 +214,9 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
 #pragma unroll
         for (int j = 0; j < FN; j++) acc[i][j] = typename T::acc_t{};
 
-    const int nk = (K + T::KSTEP - 1) / T::KSTEP;
+    // K-steps per group (with KS = 2 the second group may run one past K:
+    // its loads read zero, so both groups meet every barrier)
+    const int nk = ((K + T::KSTEP - 1) / T::KSTEP + KS - 1) / KS;
 #pragma unroll
     for (int p = 0; p < 4; p++) load_part(0, p, 0);
 #pragma unroll
@@ -237,11 +248,11 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
     auto kstep = [&](int kt, auto set_c) {
         constexpr int set = decltype(set_c)::value;
         const int cur = kt & 1;
-        const char* L = lds[cur];
+        const char* L = glds[cur];
 #pragma unroll
         for (int p = 0; p < 4; p++) {
             if (p < 3) read_frags(L, p + 1, (p + 1) & 1);
-            else read_frags(lds[cur ^ 1], 0, 0);   // the next tile's first sub-step: visible since the barrier
+            else read_frags(glds[cur ^ 1], 0, 0);   // the next tile's first sub-step: visible since the barrier
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
             if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
         }
     };
-    read_frags(lds[0], 0, 0);
+    read_frags(glds[0], 0, 0);
     if constexpr (NSET == 2) {
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
@@ -275,6 +286,42 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
         if (kt < nk) kstep(kt, std::integral_constant<int, 1>{});
     } else {
         for (int kt = 0; kt < nk; kt++) kstep(kt, std::integral_constant<int, 0>{});
+    }
+
+    if constexpr (KS == 2) {
+        // Group 1 parks its partial sums in LDS past group 0's epilogue
+        // staging area; group 0 adds them (one fixed order: the result does
+        // not depend on timing) and runs the epilogue alone.
+        constexpr int STAGE_BYTES = WM * WN * 32 * (WTN + 8) * 4;
+        constexpr int PARK_BYTES = WM * WN * FM * FN * 16 * WAVE * 4;
+        static_assert(STAGE_BYTES + PARK_BYTES <= (int)sizeof(lds), "K-split partial sums must fit in LDS");
+        uint32_t* park = reinterpret_cast<uint32_t*>(&lds[0][0] + STAGE_BYTES) + wave * FM * FN * 16 * WAVE + lane;
+        __syncthreads();   // every wave is done with the tile buffers
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const auto v = acc[i][j][r];
+                        park[((i * FN + j) * 16 + r) * WAVE] = __builtin_bit_cast(uint32_t, v);
+                    }
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const uint32_t v = park[((i * FN + j) * 16 + r) * WAVE];
+                    if constexpr (MODE == 0)
+                        acc[i][j][r] += (int32_t)v;
+                    else
+                        acc[i][j][r] += __builtin_bit_cast(float, v);
+                }
     }
 
     // Epilogue.  Each wave stages one 32-row block-row of its raw accumulators
@@ -413,7 +460,7 @@ __global__ __launch_bounds__(WM * WN * WAVE) void gemm_tiled_kernel(const void* 
 namespace {
 
 struct TileCfg {
-    int bm, bn, wm, wn;
+    int bm, bn, wm, wn, ks;  // ks: K groups per workgroup (workgroup = wm x wn x ks waves)
     float eff[4];  // sustained throughput of one full wave of such tiles, per mode (relative units)
 };
 
@@ -433,12 +480,16 @@ struct TileCfg {
 // W8A16, +2 % W16A16, equal for W4A16).  Every entry was then scaled by the
 // measured gain of the pinned schedule (geomean over the same shapes).
 constexpr TileCfg kTiles[] = {
-    {256, 192, 4, 3, {4304.f, 2521.f, 2432.f, 2504.f}}, {256, 256, 4, 4, {4701.f, 2640.f, 2560.f, 2736.f}},
-    {256, 192, 4, 2, {3927.f, 2397.f, 2187.f, 2483.f}}, {256, 128, 4, 2, {3344.f, 2122.f, 2008.f, 2130.f}},
-    {128, 256, 2, 4, {3470.f, 2126.f, 1833.f, 2127.f}}, {128, 192, 2, 2, {2388.f, 1528.f, 1496.f, 1643.f}},
-    {128, 128, 2, 2, {2683.f, 1889.f, 1577.f, 1894.f}}, {64, 192, 2, 2, {2335.f, 1379.f, 1140.f, 1406.f}},
-    {128, 64, 2, 2, {2235.f, 1335.f, 1222.f, 1353.f}},  {64, 128, 2, 2, {2292.f, 1290.f, 1105.f, 1340.f}},
-    {64, 64, 2, 2, {2076.f, 1182.f, 960.f, 1153.f}}};
+    {256, 192, 4, 3, 1, {4304.f, 2521.f, 2432.f, 2504.f}}, {256, 256, 4, 4, 1, {4701.f, 2640.f, 2560.f, 2736.f}},
+    {256, 192, 4, 2, 1, {3927.f, 2397.f, 2187.f, 2483.f}}, {256, 128, 4, 2, 1, {3344.f, 2122.f, 2008.f, 2130.f}},
+    {128, 256, 2, 4, 1, {3470.f, 2126.f, 1833.f, 2127.f}}, {128, 192, 2, 2, 1, {2388.f, 1528.f, 1496.f, 1643.f}},
+    {128, 128, 2, 2, 1, {2683.f, 1889.f, 1577.f, 1894.f}}, {64, 192, 2, 2, 1, {2335.f, 1379.f, 1140.f, 1406.f}},
+    {128, 64, 2, 2, 1, {2235.f, 1335.f, 1222.f, 1353.f}},  {64, 128, 2, 2, 1, {2292.f, 1290.f, 1105.f, 1340.f}},
+    {64, 64, 2, 2, 1, {2076.f, 1182.f, 960.f, 1153.f}},
+    // two K groups: the 4-wave entries scaled by what the split measured
+    // where it applies (one workgroup per CU, K >= 1024): W8A16 / W4A16
+    // +12-16 % (+20 % at K = 6144 and 8192), W16A16 +1-2 %, W8A8 -2-5 %
+    {64, 192, 2, 2, 2, {2218.f, 1600.f, 1322.f, 1420.f}}, {128, 128, 2, 2, 2, {2629.f, 2116.f, 1814.f, 1932.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -451,19 +502,22 @@ int num_cus() {
     return cus;
 }
 
-const TileCfg& pick_tile(int mode, int M, int N) {
-    const char* env = getenv("ARIA_QLINEAR_TILE");  // "BMxBNxWMxWN" tuning override
+const TileCfg& pick_tile(int mode, int M, int N, int K) {
+    const char* env = getenv("ARIA_QLINEAR_TILE");  // "BMxBNxWMxWN[xKS]" tuning override
     if (env) {
-        int bm = 0, bn = 0, wm = 0, wn = 0;
-        if (sscanf(env, "%dx%dx%dx%d", &bm, &bn, &wm, &wn) == 4)
+        int bm = 0, bn = 0, wm = 0, wn = 0, ks = 1;
+        if (sscanf(env, "%dx%dx%dx%dx%d", &bm, &bn, &wm, &wn, &ks) >= 4)
             for (const TileCfg& t : kTiles)
-                if (t.bm == bm && t.bn == bn && t.wm == wm && t.wn == wn) return t;
+                if (t.bm == bm && t.bn == bn && t.wm == wm && t.wn == wn && t.ks == ks) return t;
     }
     const int cus = num_cus();
     double best = 1e300;
     const TileCfg* pick = &kTiles[0];
     for (const TileCfg& t : kTiles) {
         const long tiles = (long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+        // the K split pays only where the 4-wave tile would leave one
+        // workgroup (one wave per SIMD) on each CU, and over a long enough K
+        if (t.ks > 1 && (tiles > cus || K < 1024)) continue;
         const long waves = (tiles + cus - 1) / cus;
         const double cost = (double)waves * t.bm * t.bn / t.eff[mode];
         if (cost < best) best = cost, pick = &t;
@@ -471,24 +525,25 @@ const TileCfg& pick_tile(int mode, int M, int N) {
     return *pick;
 }
 
-template <int MODE, int BM, int BN, int WM, int WN>
+template <int MODE, int BM, int BN, int WM, int WN, int KS>
 hipError_t launch_one(const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y, int M, int N,
                       int K, const Epi& e, hipStream_t st) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_tiled_kernel<MODE, BM, BN, WM, WN>), dim3(tiles), dim3(WM * WN * WAVE), 0, st, a, b, s,
-                       sa, y, M, N, K, e);
+    hipLaunchKernelGGL((gemm_tiled_kernel<MODE, BM, BN, WM, WN, KS>), dim3(tiles), dim3(WM * WN * KS * WAVE), 0, st, a,
+                       b, s, sa, y, M, N, K, e);
     return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y,
                        int M, int N, int K, const Epi& e, hipStream_t st) {
-#define ARIA_TILE(BM_, BN_, WM_, WN_)                          \
-    if (t.bm == BM_ && t.bn == BN_ && t.wm == WM_ && t.wn == WN_) \
-        return launch_one<MODE, BM_, BN_, WM_, WN_>(a, b, s, sa, y, M, N, K, e, st);
-    ARIA_TILE(256, 192, 4, 3) ARIA_TILE(256, 256, 4, 4) ARIA_TILE(256, 192, 4, 2) ARIA_TILE(256, 128, 4, 2) ARIA_TILE(128, 256, 2, 4)
-    ARIA_TILE(128, 192, 2, 2) ARIA_TILE(128, 128, 2, 2) ARIA_TILE(64, 192, 2, 2) ARIA_TILE(128, 64, 2, 2)
-    ARIA_TILE(64, 128, 2, 2) ARIA_TILE(64, 64, 2, 2)
+#define ARIA_TILE(BM_, BN_, WM_, WN_, KS_)                                     \
+    if (t.bm == BM_ && t.bn == BN_ && t.wm == WM_ && t.wn == WN_ && t.ks == KS_) \
+        return launch_one<MODE, BM_, BN_, WM_, WN_, KS_>(a, b, s, sa, y, M, N, K, e, st);
+    ARIA_TILE(256, 192, 4, 3, 1) ARIA_TILE(256, 256, 4, 4, 1) ARIA_TILE(256, 192, 4, 2, 1) ARIA_TILE(256, 128, 4, 2, 1)
+    ARIA_TILE(128, 256, 2, 4, 1) ARIA_TILE(128, 192, 2, 2, 1) ARIA_TILE(128, 128, 2, 2, 1) ARIA_TILE(64, 192, 2, 2, 1)
+    ARIA_TILE(128, 64, 2, 2, 1) ARIA_TILE(64, 128, 2, 2, 1) ARIA_TILE(64, 64, 2, 2, 1)
+    ARIA_TILE(64, 192, 2, 2, 2) ARIA_TILE(128, 128, 2, 2, 2)
 #undef ARIA_TILE
     return hipErrorInvalidValue;
 }
@@ -500,7 +555,7 @@ hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half
     // 32-bit buffer offsets: split very tall problems into row blocks
     const int64_t aeb = mode == 0 ? 1 : 2;
     const int64_t max_rows = ((int64_t)1 << 31) / ((int64_t)K * aeb) / 256 * 256;
-    const TileCfg& t = pick_tile(mode, M > max_rows ? (int)max_rows : M, N);
+    const TileCfg& t = pick_tile(mode, M > max_rows ? (int)max_rows : M, N, K);
     const uint8_t* b = static_cast<const uint8_t*>(bq);
     for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
         const int rows = (int)((M - r0) < max_rows ? (M - r0) : max_rows);

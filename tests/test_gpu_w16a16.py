@@ -100,7 +100,9 @@ def test_w16a16_full_width_m2048(q):
 
 
 TILES = ["256x192x4x3", "256x256x4x4", "256x192x4x2", "256x128x4x2", "128x256x2x4", "128x192x2x2", "128x128x2x2",
-         "64x192x2x2", "128x64x2x2", "64x128x2x2", "64x64x2x2"]
+         "64x192x2x2", "128x64x2x2", "64x128x2x2", "64x64x2x2",
+         # two K groups per workgroup (the fifth number)
+         "64x192x2x2x2", "128x128x2x2x2"]
 
 
 @pytest.mark.parametrize("tile", TILES)
