@@ -341,6 +341,27 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     const float alpha = load_alpha(epi);
     const bool vec_ok = (N % 8) == 0;
     const v8h zero8 = {};
+    // When the wave's row of chunks divides the wave (64-column wave tiles),
+    // every task of a lane covers the same 8 columns: their scales, bias and
+    // steering vector are then read and converted once per lane, not once
+    // per task and block-row.
+    constexpr bool COLFIX = WAVE % CPRW == 0;
+    const int colf = n0 + wn * WTN + (lane % CPRW) * 8;
+    const bool cvalid = COLFIX && vec_ok && colf + 8 <= N;
+    float swf[8], bf[8], df[8];
+    if constexpr (COLFIX) {
+        const v8h s8 = ((MODE == 0 || MODE == 1) && cvalid) ? *reinterpret_cast<const v8h*>(S + colf) : zero8;
+        const v8h b8 = (epi.bias && cvalid) ? *reinterpret_cast<const v8h*>(epi.bias + colf) : zero8;
+        const v4f z4 = {};
+        const v4f d0 = (alpha != 0.0f && cvalid) ? *reinterpret_cast<const v4f*>(epi.steer_dir + colf) : z4;
+        const v4f d1 = (alpha != 0.0f && cvalid) ? *reinterpret_cast<const v4f*>(epi.steer_dir + colf + 4) : z4;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            swf[e] = (float)s8[e];
+            bf[e] = (float)b8[e];
+            df[e] = e < 4 ? d0[e] : d1[e - 4];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; i++) {
         // 1) issue this round's per-element operand loads (column scales,
@@ -355,7 +376,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
             const int row = m0 + wm * WTM + i * 32 + rr, col = n0 + wn * WTN + cc * 8;
             const bool v = vec_ok && row < M && col + 8 <= N;
             const int64_t base = (int64_t)row * N + col;
-            sw8[t] = ((MODE == 0 || MODE == 1) && v) ? *reinterpret_cast<const v8h*>(S + col) : zero8;
+            sw8[t] = ((MODE == 0 || MODE == 1) && v && !COLFIX) ? *reinterpret_cast<const v8h*>(S + col) : zero8;
             sr[t] = (MODE == 0 && v) ? (float)sa[row] : 0.0f;
             r8[t] = (epi.residual && v) ? *reinterpret_cast<const v8h*>(epi.residual + base) : zero8;
         }
@@ -395,18 +416,24 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
                         reinterpret_cast<v4u*>(epi.acc_out + base)[1] = v4u{raw[4], raw[5], raw[6], raw[7]};
                     }
 #pragma unroll
-                    for (int e = 0; e < 8; e++) v[e] = (float)(int32_t)raw[e] * sr[t] * (float)sw8[t][e];
+                    for (int e = 0; e < 8; e++)
+                        v[e] = (float)(int32_t)raw[e] * sr[t] * (COLFIX ? swf[e] : (float)sw8[t][e]);
                 } else if constexpr (MODE == 1) {
 #pragma unroll
-                    for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]) * (float)sw8[t][e];
+                    for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]) * (COLFIX ? swf[e] : (float)sw8[t][e]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; e++) v[e] = __builtin_bit_cast(float, raw[e]);
                 }
                 if (epi.bias) {
-                    const v8h b8 = *reinterpret_cast<const v8h*>(epi.bias + col);
+                    if constexpr (COLFIX) {
 #pragma unroll
-                    for (int e = 0; e < 8; e++) v[e] += (float)b8[e];
+                        for (int e = 0; e < 8; e++) v[e] += bf[e];
+                    } else {
+                        const v8h b8 = *reinterpret_cast<const v8h*>(epi.bias + col);
+#pragma unroll
+                        for (int e = 0; e < 8; e++) v[e] += (float)b8[e];
+                    }
                 }
                 if (epi.gelu) {
 #pragma unroll
@@ -417,12 +444,17 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
                     for (int e = 0; e < 8; e++) v[e] += (float)r8[t][e];
                 }
                 if (alpha != 0.0f) {
-                    const v4f d0 = *reinterpret_cast<const v4f*>(epi.steer_dir + col);
-                    const v4f d1 = *reinterpret_cast<const v4f*>(epi.steer_dir + col + 4);
+                    if constexpr (COLFIX) {
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        v[e] += alpha * d0[e];
-                        v[e + 4] += alpha * d1[e];
+                        for (int e = 0; e < 8; e++) v[e] += alpha * df[e];
+                    } else {
+                        const v4f d0 = *reinterpret_cast<const v4f*>(epi.steer_dir + col);
+                        const v4f d1 = *reinterpret_cast<const v4f*>(epi.steer_dir + col + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            v[e] += alpha * d0[e];
+                            v[e + 4] += alpha * d1[e];
+                        }
                     }
                 }
                 v8h out;
