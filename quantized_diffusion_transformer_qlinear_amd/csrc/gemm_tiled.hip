@@ -133,7 +133,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     // W4A16 12-wave tile and the 16-wave tile outside W8A8 lose 3-5 % with it,
     // so they keep the free schedule.  The 4-wave tiles (two register sets)
     // always pin.
-    constexpr bool PIN = NSET == 2 || WM * WN == 8 || MODE == 0 || (WM * WN == 12 && MODE != 2);
+    constexpr bool PIN = NSET >= 2 || WM * WN == 8 || MODE == 0 || (WM * WN == 12 && MODE != 2);
     v4i RA[NSET][LA], RB[NSET][LB > 0 ? LB : 1];
     half_t RS[NSET][LB > 0 ? LB : 1];
 
@@ -222,12 +222,11 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     for (int p = 0; p < 4; p++) load_part(0, p, 0);
 #pragma unroll
     for (int p = 0; p < 4; p++) store_part(0, p, 0);
+    // tiles 1 .. NSET into register sets n % NSET (tile t lives in set t % NSET)
 #pragma unroll
-    for (int p = 0; p < 4; p++) load_part(1, p, NSET - 1);
-    if constexpr (NSET == 2) {
+    for (int n = 1; n <= NSET; n++)
 #pragma unroll
-        for (int p = 0; p < 4; p++) load_part(2, p, 0);
-    }
+        for (int p = 0; p < 4; p++) load_part(n, p, n % NSET);
     __syncthreads();
 
     const int arow = (wm * WTM + lane % 32) * ROWB + (lane / 32) * 16;
@@ -278,15 +277,20 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
         }
     };
     read_frags(glds[0], 0, 0);
+    // K-step kt stores tile kt + 1 from set (kt + 1) % NSET: unrolled by NSET
+    // (a third set for the 4-wave tiles measured 1-7 % slower)
+    static_assert(NSET == 1 || NSET == 2, "register sets");
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1 % NSET>;
     if constexpr (NSET == 2) {
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
-            kstep(kt, std::integral_constant<int, 1>{});
-            kstep(kt + 1, std::integral_constant<int, 0>{});
+            kstep(kt, S1{});
+            kstep(kt + 1, S0{});
         }
-        if (kt < nk) kstep(kt, std::integral_constant<int, 1>{});
+        if (kt < nk) kstep(kt, S1{});
     } else {
-        for (int kt = 0; kt < nk; kt++) kstep(kt, std::integral_constant<int, 0>{});
+        for (int kt = 0; kt < nk; kt++) kstep(kt, S0{});
     }
 
     if constexpr (KS == 2) {
