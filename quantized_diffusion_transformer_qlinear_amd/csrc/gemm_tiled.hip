@@ -17,16 +17,19 @@
 // LDS as rows of 128 bytes (128 int8 k or 64 fp16 k) plus a 16-byte pad that
 // spreads the 32 rows of an operand fragment over all banks; a K-step is 4
 // MFMA sub-steps in every mode.  Tiles are fetched two K-steps ahead (three
-// for 4-wave tiles) into registers with bounds-checked buffer loads (rows past
-// M/N and k past K read as zero), and the decode + LDS store of the next one
-// is split over the first 3 sub-steps of the current K-step so that it
-// overlaps the matrix work.  The one barrier per K-step comes after the third
-// sub-step: the next tile is then complete in LDS, and its first fragments are
-// read while the last sub-step's MFMAs run (a barrier at the end of the K-step
-// left every wave waiting on those reads with nothing to issue).  Packed
-// weights are decoded in registers: int8 -> fp16 and nibble -> fp16 by
-// building the fp16 pattern 0x6400 | u (= 1024 + u) and subtracting the bias,
-// two values per packed-half instruction.
+// with a second register set: 4-wave tiles and the 12-wave W8A16 tile) into
+// registers with bounds-checked buffer loads (rows past M/N and k past K read
+// as zero), and the decode + LDS store of the next one is split over the
+// first 3 sub-steps of the current K-step so that it overlaps the matrix
+// work (for most tiles pinned there by scheduling barriers, see PIN).  The
+// one barrier per K-step comes after the third sub-step: the next tile is
+// then complete in LDS, and its first fragments are read while the last
+// sub-step's MFMAs run (a barrier at the end of the K-step left every wave
+// waiting on those reads with nothing to issue).  Packed weights are decoded
+// in registers (decode.h: fp16 patterns 0x6400 | u and, for the high nibble,
+// 0x5400 | u << 4, minus their offsets), two values per packed-half
+// instruction.  The epilogue stages the accumulators through LDS and writes
+// 16-byte rows of fp16 with non-temporal stores.
 #include <type_traits>
 
 #include "common.h"
