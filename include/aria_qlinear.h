@@ -120,8 +120,13 @@ typedef struct aria_epilogue {
 } aria_epilogue;
 
 /* Workspace (device bytes) the qlinear call needs for this shape; 0 = none.
- * W8A8 needs room for Xq int8 [M][K] and s_a fp16 [M]; the weight-only modes
- * need room for split-K partial sums at small M. */
+ * W8A8 needs room for Xq int8 [M][K] and s_a fp16 [M] (256-byte aligned
+ * parts); the weight-only modes currently need none, but callers should query
+ * rather than assume.
+ *
+ * Tile choice (M > 64) is automatic; the environment variable
+ * ARIA_QLINEAR_TILE="BMxBNxWMxWN[xKS]" forces one of the library's tile
+ * variants (a tuning and testing override; an unknown value is ignored). */
 size_t aria_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, int64_t N);
 
 /* a2+a4+a5 — W8A8: Y = epilogue( (sum_k Xq[m][k] * Wq[n][k]) * s_a[m] * s_w[n] )
