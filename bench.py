@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "qlinear TOPS + % of MFMA/HBM roofline (W8A8, W8A16, W4A16) at M=2048"
 PEAK = {"int8": 5000.0, "fp16": 2500.0, "hbm": 8000.0}  # TOPS, TFLOP/s, GB/s (MI355X datasheet, dense)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_dit_qlinear_m2048.txt")
-KERNEL_SOURCES = ["common.h", "decode.h", "gemm_tiled.hip", "gemm_skinny.hip", "actquant.hip"]
+KERNEL_SOURCES = ["common.h", "decode.h", "rowops.h", "gemm_tiled.hip", "gemm_skinny.hip", "actquant.hip"]
 
 
 def kernel_hash() -> str:
@@ -257,9 +257,10 @@ def precision_ladder(q, torch, dev, lin2, x_small, reps=20):
 
 
 def full_block(q, torch, dev, si, blk, packed, reps=20):
-    """The W8A8 DiT block with its attention core and pre-norms (LN1, QKV,
-    attention over 2 x 1024 tokens with 24 heads of 64, out + residual, LN2,
-    MLP-up + GELU, MLP-down + residual + alpha*d) at M = 2048: graph-replayed
+    """The W8A8 DiT block with its attention core and pre-norms (LN1 fused
+    with the QKV input's quantization, QKV, attention over 2 x 1024 tokens
+    with 24 heads of 64, out + residual, LN2 fused with the MLP-up input's
+    quantization, MLP-up + GELU, MLP-down + residual + alpha*d) at M = 2048: graph-replayed
     microseconds per block and a per-stage breakdown (each stage alone, graph-replayed)."""
     from quantized_diffusion_transformer_qlinear_amd.chain import DitBlockFullW8A8
     norms = si.dit_block_norms()

@@ -172,6 +172,25 @@ int aria_qlinear_w16a16(const void* x_f16, int64_t M, int64_t K, int64_t N, cons
 int aria_layernorm(const void* x_f16, int64_t M, int64_t W, const void* gamma_f16, const void* beta_f16,
                    float eps, void* y_f16, aria_stream_t stream);
 
+/* LayerNorm as aria_layernorm, then the per-token quantization of its fp16
+ * result as aria_quant_act, in one pass that keeps each row in registers: the
+ * pre-norm in front of a W8A8 linear.  Xq int8 [M][W] and s_a fp16 [M] are
+ * bit-identical to aria_layernorm followed by aria_quant_act on its output;
+ * y (fp16 [M][W], the normalized rows) may be NULL when only the quantized
+ * form is needed, or x (in place).  Shape rules are those of a W8A8 linear
+ * with K = W (32 <= W <= 16384, W % 32 == 0); 0 <= eps <= 1.  xq and s_a must
+ * not overlap x, y or each other. */
+int aria_layernorm_quant(const void* x_f16, int64_t M, int64_t W, const void* gamma_f16, const void* beta_f16,
+                         float eps, void* y_f16, int8_t* xq, void* s_a_f16, aria_stream_t stream);
+
+/* a4+a5 — the W8A8 linear on activations quantized beforehand (by
+ * aria_quant_act or aria_layernorm_quant): the GEMM and epilogue of
+ * aria_qlinear_w8a8 without its quantization step, so the same Xq / s_a give
+ * the same Y bit for bit.  Needs no workspace; xq and s_a must not overlap y. */
+int aria_qlinear_w8a8_prequant(const int8_t* xq, const void* s_a_f16, int64_t M, int64_t K, int64_t N,
+                               const int8_t* wq, const void* s_w_f16, const aria_epilogue* epi,
+                               void* y_f16, aria_stream_t stream);
+
 /* Multi-head softmax self-attention: qkv fp16 [M][3W] holds [Q | K | V]
  * column blocks (the QKV linear's output), head h of each at columns
  * h*64 .. h*64+63; the M rows are M / seq independent sequences of seq rows.

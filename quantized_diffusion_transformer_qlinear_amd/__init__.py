@@ -9,7 +9,7 @@ convenience, allocates outputs with torch.  There is no fallback: importing
 the binding without the built library raises.
 """
 from .binding import (  # noqa: F401
-    ARIA_W4A16, ARIA_W8A16, ARIA_W8A8, ARIA_W16A16, AriaError, attention, layernorm, lib, library_path,
-    qlinear_grouped, qlinear_w4a16, qlinear_w8a8, qlinear_w8a16, qlinear_w16a16, qpack, qpack_bytes, quant_act,
-    status_string, workspace_bytes,
+    ARIA_W4A16, ARIA_W8A16, ARIA_W8A8, ARIA_W16A16, AriaError, attention, layernorm, layernorm_quant, lib,
+    library_path, qlinear_grouped, qlinear_w4a16, qlinear_w8a8, qlinear_w8a8_prequant, qlinear_w8a16,
+    qlinear_w16a16, qpack, qpack_bytes, quant_act, status_string, workspace_bytes,
 )

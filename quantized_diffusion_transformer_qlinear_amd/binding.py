@@ -47,6 +47,10 @@ lib.aria_qlinear_w16a16.restype = _I
 
 lib.aria_layernorm.argtypes = [_P, _I64, _I64, _P, _P, ctypes.c_float, _P, _P]
 lib.aria_layernorm.restype = _I
+lib.aria_layernorm_quant.argtypes = [_P, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P, _P]
+lib.aria_layernorm_quant.restype = _I
+lib.aria_qlinear_w8a8_prequant.argtypes = [_P, _P, _I64, _I64, _I64, _P, _P, ctypes.POINTER(Epilogue), _P, _P]
+lib.aria_qlinear_w8a8_prequant.restype = _I
 lib.aria_attention.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P]
 lib.aria_attention.restype = _I
 
@@ -252,6 +256,38 @@ def layernorm(x, gamma, beta, eps: float = 1e-5, y=None, stream=None):
     y = torch.empty_like(x) if y is None else y
     _check(lib.aria_layernorm(_addr(x), M, W, _addr(gamma), _addr(beta), float(eps), _addr(y), _stream(stream)),
            "layernorm")
+    return y
+
+
+def layernorm_quant(x, gamma, beta, eps: float = 1e-5, y=None, xq=None, sa=None, want_y: bool = False,
+                    stream=None):
+    """LayerNorm of x fp16 [M][W] and the per-token quantization of the
+    result in one pass: returns (xq, sa) or, with want_y / a given y,
+    (y, xq, sa)."""
+    torch = _torch()
+    _dt(x, torch.float16, "x"), _dt(gamma, torch.float16, "gamma"), _dt(beta, torch.float16, "beta")
+    M, W = x.shape
+    if y is None and want_y:
+        y = torch.empty_like(x)
+    xq = torch.empty((M, W), dtype=torch.int8, device=x.device) if xq is None else xq
+    sa = torch.empty((M,), dtype=torch.float16, device=x.device) if sa is None else sa
+    _check(lib.aria_layernorm_quant(_addr(x), M, W, _addr(gamma), _addr(beta), float(eps), _addr(y), _addr(xq),
+                                    _addr(sa), _stream(stream)), "layernorm_quant")
+    return (xq, sa) if y is None else (y, xq, sa)
+
+
+def qlinear_w8a8_prequant(xq, sa, wq, sw, y=None, bias=None, gelu=False, residual=None, steer_dir=None,
+                          steer_alpha=None, acc_out=None, stream=None):
+    """The W8A8 linear on activations quantized beforehand (xq int8 [M][K],
+    sa fp16 [M])."""
+    torch = _torch()
+    _dt(xq, torch.int8, "xq"), _dt(sa, torch.float16, "sa"), _dt(wq, torch.int8, "wq"), _dt(sw, torch.float16, "sw")
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = torch.empty((M, N), dtype=torch.float16, device=xq.device) if y is None else y
+    e = _epi(bias, gelu, residual, steer_dir, steer_alpha, acc_out)
+    _check(lib.aria_qlinear_w8a8_prequant(_addr(xq), _addr(sa), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e),
+                                          _addr(y), _stream(stream)), "qlinear_w8a8_prequant")
     return y
 
 

@@ -86,21 +86,26 @@ class DitBlockFullW8A8:
       n2 = LN2(h1); u = gelu(n2.Wup); out = h1 + u.Wdown + alpha*d,
     with `heads` 64-dimensional heads over sequences of `seq` tokens (the M
     rows hold M / seq sequences, e.g. two guidance branches).  Every step runs
-    in the library's kernels; ``run(h)`` returns the block output."""
+    in the library's kernels; ``run(h)`` returns the block output.  Each
+    pre-norm is fused with the per-token quantization of the W8A8 linear it
+    feeds (the normalized rows stay in registers); ``keep_norms`` also writes
+    the fp16 normalized rows to ``n1`` / ``n2`` for inspection."""
 
     def __init__(self, packed: dict, ln1, ln2, M: int, width: int, mlp: int, heads: int, seq: int,
-                 steer_dir=None, steer_alpha=None, eps: float = 1e-5):
+                 steer_dir=None, steer_alpha=None, eps: float = 1e-5, keep_norms: bool = False):
         import torch
         dev = packed["qkv"][0].device
         self.packed, self.ln1, self.ln2, self.eps = packed, ln1, ln2, eps
         self.M, self.width, self.mlp, self.heads, self.seq = M, width, mlp, heads, seq
         self.steer_dir, self.steer_alpha = steer_dir, steer_alpha
         f16 = torch.float16
-        self.n1 = torch.empty((M, width), dtype=f16, device=dev)
+        self.n1 = torch.empty((M, width), dtype=f16, device=dev) if keep_norms else None
+        self.n2 = torch.empty((M, width), dtype=f16, device=dev) if keep_norms else None
+        self.xq = torch.empty((M, width), dtype=torch.int8, device=dev)   # quantized n1, then n2
+        self.sa = torch.empty((M,), dtype=f16, device=dev)
         self.qkv = torch.empty((M, 3 * width), dtype=f16, device=dev)
         self.a = torch.empty((M, width), dtype=f16, device=dev)
         self.h1 = torch.empty((M, width), dtype=f16, device=dev)
-        self.n2 = torch.empty((M, width), dtype=f16, device=dev)
         self.u = torch.empty((M, mlp), dtype=f16, device=dev)
         self.out = torch.empty((M, width), dtype=f16, device=dev)
         need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, 1) for k in (width, mlp))
@@ -110,12 +115,15 @@ class DitBlockFullW8A8:
         """The stages as (name, callable) pairs, in order (see DitBlockW8A8.calls)."""
         p = self.packed
         return [
-            ("ln1", lambda: B.layernorm(h, *self.ln1, eps=self.eps, y=self.n1, stream=stream)),
-            ("qkv", lambda: B.qlinear_w8a8(self.n1, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)),
+            ("ln1", lambda: B.layernorm_quant(h, *self.ln1, eps=self.eps, y=self.n1, xq=self.xq, sa=self.sa,
+                                              stream=stream)),
+            ("qkv", lambda: B.qlinear_w8a8_prequant(self.xq, self.sa, *p["qkv"], y=self.qkv, stream=stream)),
             ("attention", lambda: B.attention(self.qkv, self.heads, self.seq, out=self.a, stream=stream)),
             ("out", lambda: B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)),
-            ("ln2", lambda: B.layernorm(self.h1, *self.ln2, eps=self.eps, y=self.n2, stream=stream)),
-            ("up", lambda: B.qlinear_w8a8(self.n2, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)),
+            ("ln2", lambda: B.layernorm_quant(self.h1, *self.ln2, eps=self.eps, y=self.n2, xq=self.xq, sa=self.sa,
+                                              stream=stream)),
+            ("up", lambda: B.qlinear_w8a8_prequant(self.xq, self.sa, *p["up"], y=self.u, gelu=True,
+                                                   stream=stream)),
             ("down", lambda: B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
                                             steer_dir=self.steer_dir, steer_alpha=self.steer_alpha,
                                             stream=stream)),

@@ -262,6 +262,41 @@ int aria_layernorm(const void* x, int64_t M, int64_t W, const void* gamma, const
                                        static_cast<hipStream_t>(stream)));
 }
 
+int aria_layernorm_quant(const void* x, int64_t M, int64_t W, const void* gamma, const void* beta, float eps,
+                         void* y, int8_t* xq, void* sa, aria_stream_t stream) {
+    // the quantized row feeds a W8A8 linear with K = W: its shape rules apply
+    if (check_shape(M, W, 1) != ARIA_OK) return ARIA_E_SHAPE;
+    if (!(eps >= 0.0f) || eps > 1.0f) return ARIA_E_UNSUPPORTED;
+    if (!x || !gamma || !beta || !xq || !sa) return ARIA_E_NULL;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || !aligned16(y) || !aligned16(xq) || !aligned16(sa))
+        return ARIA_E_ALIGN;
+    const size_t xb = (size_t)(M * W) * 2;
+    if (overlap(x, xb, xq, (size_t)(M * W)) || overlap(x, xb, sa, (size_t)M * 2) ||
+        overlap(xq, (size_t)(M * W), sa, (size_t)M * 2) ||
+        (y && y != x && overlap(x, xb, y, xb)) || (y && (overlap(y, xb, xq, (size_t)(M * W)) || overlap(y, xb, sa, (size_t)M * 2))))
+        return ARIA_E_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(launch_layernorm_quant(static_cast<const half_t*>(x), static_cast<const half_t*>(gamma),
+                                             static_cast<const half_t*>(beta), eps, M, W, static_cast<half_t*>(y), xq,
+                                             static_cast<half_t*>(sa), static_cast<hipStream_t>(stream)));
+}
+
+int aria_qlinear_w8a8_prequant(const int8_t* xq, const void* s_a, int64_t M, int64_t K, int64_t N, const int8_t* wq,
+                               const void* sw, const aria_epilogue* epi, void* y, aria_stream_t stream) {
+    int rc = check_shape(M, K, N);
+    if (rc != ARIA_OK) return rc;
+    if (!xq || !s_a || !wq || !sw || !y) return ARIA_E_NULL;
+    if (!aligned16(xq) || !aligned16(s_a) || !aligned16(wq) || !aligned16(sw) || !aligned16(y)) return ARIA_E_ALIGN;
+    const size_t yb = (size_t)(M * N) * 2;
+    if (overlap(xq, (size_t)(M * K), y, yb) || overlap(s_a, (size_t)M * 2, y, yb)) return ARIA_E_ALIAS;
+    Epi e;
+    if ((rc = make_epi(epi, ARIA_W8A8, M, N, y, &e)) != ARIA_OK) return rc;
+    (void)hipGetLastError();
+    return hip_status(launch_gemm_tiled(0, xq, wq, static_cast<const half_t*>(sw), static_cast<const half_t*>(s_a),
+                                        static_cast<half_t*>(y), (int)M, (int)N, (int)K, e,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int aria_attention(const void* qkv, int64_t M, int64_t W, int64_t heads, int64_t seq, void* out, aria_stream_t stream) {
     if (M < 1 || M > kMaxDim || heads < 1 || seq < 1 || M % seq != 0) return ARIA_E_SHAPE;
     if (W != heads * 64) return ARIA_E_UNSUPPORTED;                      // 64-dimensional heads only

@@ -13,6 +13,9 @@ hipError_t launch_pack16(const half_t* w, int64_t K, int64_t N, half_t* wt, hipS
 // The DiT block's steps around the linears (layernorm.hip, attention.hip).
 hipError_t launch_layernorm(const half_t* x, const half_t* gamma, const half_t* beta, float eps, int64_t M, int64_t W,
                             half_t* y, hipStream_t st);
+// LayerNorm then per-token quantization of its fp16 output (y may be null).
+hipError_t launch_layernorm_quant(const half_t* x, const half_t* gamma, const half_t* beta, float eps, int64_t M,
+                                  int64_t W, half_t* y, int8_t* xq, half_t* sa, hipStream_t st);
 hipError_t launch_attention(const half_t* qkv, int64_t M, int64_t W, int64_t H, int64_t S, half_t* out,
                             hipStream_t st);
 

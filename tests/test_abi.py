@@ -29,7 +29,7 @@ def q():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (aria_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -120,6 +120,23 @@ def test_validation_codes(q):
     assert L.aria_layernorm(X, 64, 256, None, S, 1e-5, Y, None) == -1
     assert L.aria_layernorm(X, 64, 256, W, S + 2, 1e-5, Y, None) == -3
     assert L.aria_layernorm(X, 64, 256, W, S, 1e-5, X + 512, None) == -7     # partial overlap
+    # fused pre-norm + quantization (W8A8 shape rules on W), and the linear on
+    # activations quantized beforehand
+    Q, SA = 6 << 20, 7 << 20
+    assert L.aria_layernorm_quant(X, 64, 80, W, S, 1e-5, None, Q, SA, None) == -2      # W % 32
+    assert L.aria_layernorm_quant(X, 64, 256, W, S, 2.0, None, Q, SA, None) == -4
+    assert L.aria_layernorm_quant(X, 64, 256, W, S, 1e-5, None, None, SA, None) == -1
+    assert L.aria_layernorm_quant(X, 64, 256, W, S, 1e-5, Y + 2, Q, SA, None) == -3
+    assert L.aria_layernorm_quant(X, 64, 256, W, S, 1e-5, None, X + 256, SA, None) == -7
+    assert L.aria_layernorm_quant(X, 64, 256, W, S, 1e-5, None, Q, Q + 64, None) == -7
+    assert L.aria_layernorm_quant(X, 64, 256, W, S, 1e-5, X + 512, Q, SA, None) == -7
+    assert L.aria_layernorm_quant(X, 64, 256, W, S, 1e-5, Y, Q, Y + 256, None) == -7
+    assert L.aria_qlinear_w8a8_prequant(Q, SA, 64, 48, 256, W, S, None, Y, None) == -2
+    assert L.aria_qlinear_w8a8_prequant(Q, None, 64, 256, 256, W, S, None, Y, None) == -1
+    assert L.aria_qlinear_w8a8_prequant(Q, SA + 2, 64, 256, 256, W, S, None, Y, None) == -3
+    assert L.aria_qlinear_w8a8_prequant(Q, SA, 64, 256, 256, W, S, None, Q + 64, None) == -7
+    ep2 = E(None, 3, 0, None, None, None, None)
+    assert L.aria_qlinear_w8a8_prequant(Q, SA, 64, 256, 256, W, S, ctypes.byref(ep2), Y, None) == -4
     assert L.aria_attention(X, 64, 96, 2, 32, Y, None) == -4                 # head dim 48
     assert L.aria_attention(X, 64, 128, 2, 48, Y, None) == -2                # M % seq
     assert L.aria_attention(None, 64, 128, 2, 32, Y, None) == -1

@@ -39,6 +39,73 @@ def test_layernorm_in_place(q):
     assert_close(host(xd), oracle.layernorm(x, g, b, 1e-5), "layernorm in place")
 
 
+@pytest.mark.parametrize("M,W", [(1, 32), (5, 96), (33, 1536), (130, 544), (3, 16384), (2051, 1536)])
+def test_layernorm_quant(q, M, W):
+    """The fused pre-norm + per-token quantization: y close to the oracle's
+    LayerNorm, xq / s_a bit-exact with the oracle's quantization of that y,
+    and all three bit-identical with the two separate kernels."""
+    rng = np.random.default_rng(M * 11 + W)
+    x = (rng.standard_normal((M, W)) * 2 + 0.5).astype(np.float16)
+    x[0, :: max(1, W // 7)] = 40.0                       # one row with outliers
+    g = (1 + 0.1 * rng.standard_normal(W)).astype(np.float16)
+    b = (0.1 * rng.standard_normal(W)).astype(np.float16)
+    log(f"layernorm_quant M={M} W={W}")
+    xd, gd, bd = dev(x), dev(g), dev(b)
+    y, xq, sa = q.layernorm_quant(xd, gd, bd, 1e-5, want_y=True)
+    yh = host(y)
+    assert_close(yh, oracle.layernorm(x, g, b, 1e-5), f"layernorm_quant y {M}x{W}")
+    xq_ref, sa_ref = oracle.quant_act(yh)
+    assert np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(host(sa).view(np.uint16), sa_ref.view(np.uint16))
+    y2 = q.layernorm(xd, gd, bd, 1e-5)
+    xq2, sa2 = q.quant_act(y2)
+    assert np.array_equal(host(y).view(np.uint16), host(y2).view(np.uint16))
+    assert np.array_equal(host(xq), host(xq2))
+    assert np.array_equal(host(sa).view(np.uint16), host(sa2).view(np.uint16))
+    xq3, sa3 = q.layernorm_quant(xd, gd, bd, 1e-5)       # no y written
+    assert np.array_equal(host(xq3), host(xq2))
+    assert np.array_equal(host(sa3).view(np.uint16), host(sa2).view(np.uint16))
+
+
+def test_layernorm_quant_in_place(q):
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((70, 1536)).astype(np.float16)
+    g, b = np.ones(1536, np.float16), np.zeros(1536, np.float16)
+    xd = dev(x)
+    _, xq, sa = q.layernorm_quant(xd, dev(g), dev(b), 1e-5, y=xd)
+    yh = host(xd)
+    assert_close(yh, oracle.layernorm(x, g, b, 1e-5), "layernorm_quant in place")
+    xq_ref, sa_ref = oracle.quant_act(yh)
+    assert np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(host(sa).view(np.uint16), sa_ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 8), (77, 1536, 4608), (2048, 1536, 6144), (300, 6144, 1536)])
+def test_w8a8_prequant_matches_w8a8(q, M, K, N):
+    """The linear on quantized-beforehand activations gives the W8A8 call's
+    output bit for bit (same Xq / s_a, same GEMM and epilogue)."""
+    import torch
+    rng = np.random.default_rng(M + K + N)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (rng.standard_normal((K, N)) * 0.05).astype(np.float16)
+    bias = (0.1 * rng.standard_normal(N)).astype(np.float16)
+    res = rng.standard_normal((M, N)).astype(np.float16)
+    d = rng.standard_normal(N).astype(np.float32)
+    alpha = torch.tensor([0.25], dtype=torch.float32, device="cuda:0")
+    log(f"w8a8_prequant M={M} K={K} N={N}")
+    wq, sw = q.qpack(8, dev(w))
+    xd = dev(x)
+    epi = dict(bias=dev(bias), gelu=True, residual=dev(res), steer_dir=dev(d), steer_alpha=alpha)
+    y_ref = q.qlinear_w8a8(xd, wq, sw, **epi)
+    xq, sa = q.quant_act(xd)
+    y = q.qlinear_w8a8_prequant(xq, sa, wq, sw, **epi)
+    assert np.array_equal(host(y).view(np.uint16), host(y_ref).view(np.uint16))
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
+    q.qlinear_w8a8_prequant(xq, sa, wq, sw, acc_out=acc)
+    rows = sample_rows(M, 16, 1)
+    assert np.array_equal(host(acc)[rows], oracle.gemm_i8(host(xq)[rows], host(wq)))
+
+
 # the last shape launches 640 workgroups, past the two-per-CU mark where the
 # kernel stops prefetching a block's fragments (both variants are covered)
 @pytest.mark.parametrize("heads,seq,M", [(1, 1, 1), (1, 64, 64), (2, 100, 200), (3, 130, 130), (2, 257, 514),
@@ -86,7 +153,7 @@ def block(q):
     ln2 = tuple(dev(a) for a in norms["ln2"])
     alpha = torch.tensor([blk["alpha"]], dtype=torch.float32, device="cuda:0")
     chain = DitBlockFullW8A8(packed, ln1, ln2, si.TOKENS, si.WIDTH, si.MLP, si.HEADS, si.SEQ,
-                             steer_dir=dev(blk["d"]), steer_alpha=alpha)
+                             steer_dir=dev(blk["d"]), steer_alpha=alpha, keep_norms=True)
     chain.run(dev(blk["h"]))
     torch.cuda.synchronize()
     return blk, norms, opacked, chain
@@ -112,6 +179,11 @@ def test_block_stagewise(block):
     log("block stage ln2")
     assert_close(host(chain.n2)[rows], oracle.layernorm(h1[rows], *norms["ln2"]), "ln2")
     n2 = host(chain.n2)
+    # the fused pre-norm's quantized rows (the up linear's input) are the
+    # oracle's per-token quantization of the normalized rows it also wrote
+    xq_ref, sa_ref = oracle.quant_act(n2[rows])
+    assert np.array_equal(host(chain.xq)[rows], xq_ref), "ln2 xq"
+    assert np.array_equal(host(chain.sa)[rows].view(np.uint16), sa_ref.view(np.uint16)), "ln2 s_a"
     log("block stage up")
     assert_close(host(chain.u)[rows], oracle.qlinear_w8a8(n2[rows], *op["up"], gelu=True)["y"], "up")
     u = host(chain.u)
