@@ -373,10 +373,14 @@ def step_1p2b(q, torch, dev, si, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the shader clock ramps up over the first ~50 steps (0.23-0.26 ms each,
+    # then a steady ~0.22 ms serial): warm up past it
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--serial", action="store_true",
+                    help="capture the step on one stream (no parallel branches)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the small-M streaming, precision-ladder, full-block and 1.2B-step measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -428,11 +432,30 @@ def main():
 
     names = ["w8a8.qkv", "attention(copy)", "w8a8.out", "w8a8.up", "w8a8.down", "w8a16.up", "w4a16"]
 
+    # The step's three groups are independent: the W8A8 chain, the W8A16
+    # layer and the W4A16 layer.  Replayed as a graph they run as parallel
+    # branches: the chain on a forked stream (captured first, so its kernels
+    # are dispatched first), the two weight-only layers on the capturing
+    # stream, joined at the end; their kernels fill the CUs the chain leaves
+    # idle (QKV's 192 tiles on 256 CUs, the act-quant passes).  Eager runs
+    # (used for kernel traces) keep one stream so every kernel runs alone.
+    side = torch.cuda.Stream()
+    concurrent = not (args.eager or args.serial)
+
     def step():
-        for _ in chain.stages(h):
-            pass
+        cur = torch.cuda.current_stream()
+        if concurrent:
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                for _ in chain.stages(h):
+                    pass
+        else:
+            for _ in chain.stages(h):
+                pass
         q.qlinear_w8a16(x2, wq2, sw2, y=y2, bias=b2, gelu=True)
         q.qlinear_w4a16(x3d, wq3, sg3, y=y3)
+        if concurrent:
+            cur.wait_stream(side)
 
     for _ in range(args.warmup):
         step()
@@ -528,7 +551,9 @@ def main():
                                "(+bias, GELU) + W4A16 g32 1536x6144",
                    "tokens": M, "width": si.WIDTH, "mlp": si.MLP, "ops_per_step": total_ops},
         "roofline": rf,
-        "timing": "HIP graph replay of the step" if graph is not None else "eager launches",
+        "timing": ("eager launches" if graph is None else
+                   "HIP graph replay of the step" + (" (W8A8 chain and weight-only layers as parallel branches)"
+                                                     if concurrent else "")),
         "modes": modes,
         "calls": calls,
     }
