@@ -307,7 +307,9 @@ def step_1p2b(q, torch, dev, si, reps=5):
     Weights are seeded N(0, 0.02) drawn on the device and packed at 8 and at 4
     bits (the fp16 copy is released after packing); the step runs at q8
     (W8A16), q4 (W4A16) and W8A8 on the q8 storage.  Each precision's 96 calls
-    are captured as one graph and replayed: ms per step, aggregate TOPS,
+    are captured as one graph, in two parallel branches (linear i on branch
+    i % 2, each branch with its own outputs and workspace; also timed on one
+    stream as `serial_ms_per_step`), and replayed: ms per step, aggregate TOPS,
     algorithmic bytes / time (packed weights + scales + X + Y per linear) and
     the resident packed footprint (measured allocation and the packed sizes)."""
     M = si.TOKENS
@@ -330,20 +332,45 @@ def step_1p2b(q, torch, dev, si, reps=5):
     gen.manual_seed(501)
     xs = {K: torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32).half()
           for K in sorted({K for _n, K, _N in si.STEP_LAYERS})}
-    ys = {N: torch.empty((M, N), dtype=torch.float16, device=dev) for N in sorted({N for _n, _K, N in si.STEP_LAYERS})}
+    nbr = 2
+    ys = [{N: torch.empty((M, N), dtype=torch.float16, device=dev) for N in sorted({N for _n, _K, N in si.STEP_LAYERS})}
+          for _ in range(nbr)]
     kmax = max(xs)
-    ws = torch.empty(max(q.workspace_bytes(q.ARIA_W8A8, M, kmax, 1), 1), dtype=torch.uint8, device=dev)
+    ws = [torch.empty(max(q.workspace_bytes(q.ARIA_W8A8, M, kmax, 1), 1), dtype=torch.uint8, device=dev)
+          for _ in range(nbr)]
     ops = sum(2.0 * M * K * N for K, N, _ in p8)
     xy = sum(2.0 * M * (K + N) for K, N, _ in p8)
-    runs = {
-        "q8 (W8A16)": (lambda: [q.qlinear_w8a16(xs[K], *pk, y=ys[N]) for K, N, pk in p8], packed8),
-        "q4 (W4A16)": (lambda: [q.qlinear_w4a16(xs[K], *pk, y=ys[N]) for K, N, pk in p4], packed4),
-        "W8A8 (q8 storage)": (lambda: [q.qlinear_w8a8(xs[K], *pk, y=ys[N], ws=ws) for K, N, pk in p8], packed8),
+    calls = {
+        "q8 (W8A16)": ([(lambda b, K=K, N=N, pk=pk: q.qlinear_w8a16(xs[K], *pk, y=ys[b][N])) for K, N, pk in p8],
+                       packed8),
+        "q4 (W4A16)": ([(lambda b, K=K, N=N, pk=pk: q.qlinear_w4a16(xs[K], *pk, y=ys[b][N])) for K, N, pk in p4],
+                       packed4),
+        "W8A8 (q8 storage)": ([(lambda b, K=K, N=N, pk=pk: q.qlinear_w8a8(xs[K], *pk, y=ys[b][N], ws=ws[b]))
+                               for K, N, pk in p8], packed8),
     }
-    res = {"linears": len(p8), "weights": sum(K * N for K, N, _ in p8), "ops_per_step": ops,
-           "resident_bytes": {"fp16 (released)": fp16_bytes, "q8": packed8, "q4": packed4,
-                              "allocated_q8_plus_q4": resident}}
-    for name, (fn, wbytes) in runs.items():
+    side = [torch.cuda.Stream() for _ in range(nbr - 1)]
+
+    def serial(fns):
+        for f in fns:
+            f(0)
+
+    def branched(fns):
+        # linear i on branch i % nbr: branch 0 on the current stream, the
+        # others on forked streams joined back at the end
+        cur = torch.cuda.current_stream()
+        for s in side:
+            s.wait_stream(cur)
+        for i, f in enumerate(fns):
+            b = i % nbr
+            if b == 0:
+                f(0)
+            else:
+                with torch.cuda.stream(side[b - 1]):
+                    f(b)
+        for s in side:
+            cur.wait_stream(s)
+
+    def replay_ms(fn):
         fn()
         g = torch.cuda.CUDAGraph()
         st = torch.cuda.Stream()
@@ -361,10 +388,17 @@ def step_1p2b(q, torch, dev, si, reps=5):
             g.replay()
         e.record()
         torch.cuda.synchronize()
-        ms = a.elapsed_time(e) / reps
-        res[name] = {"ms_per_step": round(ms, 3), "tops": round(ops / ms / 1e9, 1),
-                     "GB/s": round((wbytes + xy) / ms / 1e6, 1)}
         del g
+        return a.elapsed_time(e) / reps
+
+    res = {"linears": len(p8), "weights": sum(K * N for K, N, _ in p8), "ops_per_step": ops, "branches": nbr,
+           "resident_bytes": {"fp16 (released)": fp16_bytes, "q8": packed8, "q4": packed4,
+                              "allocated_q8_plus_q4": resident}}
+    for name, (fns, wbytes) in calls.items():
+        ms_serial = replay_ms(lambda: serial(fns))
+        ms = replay_ms(lambda: branched(fns))
+        res[name] = {"ms_per_step": round(ms, 3), "tops": round(ops / ms / 1e9, 1),
+                     "GB/s": round((wbytes + xy) / ms / 1e6, 1), "serial_ms_per_step": round(ms_serial, 3)}
     del p8, p4, xs, ys, ws
     torch.cuda.synchronize()
     return res
