@@ -335,9 +335,8 @@ def step_1p2b(q, torch, dev, si, reps=5):
     nbr = 2
     ys = [{N: torch.empty((M, N), dtype=torch.float16, device=dev) for N in sorted({N for _n, _K, N in si.STEP_LAYERS})}
           for _ in range(nbr)]
-    kmax = max(xs)
-    ws = [torch.empty(max(q.workspace_bytes(q.ARIA_W8A8, M, kmax, 1), 1), dtype=torch.uint8, device=dev)
-          for _ in range(nbr)]
+    wsb = max(max(q.workspace_bytes(q.ARIA_W8A8, M, K, N) for _n, K, N in si.STEP_LAYERS), 1)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(nbr)]
     ops = sum(2.0 * M * K * N for K, N, _ in p8)
     xy = sum(2.0 * M * (K + N) for K, N, _ in p8)
     calls = {

@@ -49,7 +49,8 @@ class DitBlockW8A8:
         self.h1 = torch.empty((M, width), dtype=f16, device=dev)
         self.u = torch.empty((M, mlp), dtype=f16, device=dev)
         self.out = torch.empty((M, width), dtype=f16, device=dev)
-        need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, 1) for k in (width, mlp))
+        need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, n)
+                   for k, n in ((width, 3 * width), (width, width), (width, mlp), (mlp, width)))
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def calls(self, h, stream=None):
@@ -108,7 +109,8 @@ class DitBlockFullW8A8:
         self.h1 = torch.empty((M, width), dtype=f16, device=dev)
         self.u = torch.empty((M, mlp), dtype=f16, device=dev)
         self.out = torch.empty((M, width), dtype=f16, device=dev)
-        need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, 1) for k in (width, mlp))
+        need = max(B.workspace_bytes(B.ARIA_W8A8, M, k, n)
+                   for k, n in ((width, 3 * width), (width, width), (width, mlp), (mlp, width)))
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def calls(self, h, stream=None):
