@@ -7,7 +7,9 @@ while streaming").  Here the W8A8 block chain plus a W8A16 and a W4A16 layer
 are captured once; every replay (with unrelated eager work in between) must
 match the eager result bit for bit, and writing a new alpha into the device
 scalar between replays must change the steered output exactly as an eager
-call with that alpha does."""
+call with that alpha does.  Captured on one stream, and as the benchmark
+captures its step: the chain on a forked stream, the weight-only layers on
+the capturing stream, as parallel branches of the graph."""
 import numpy as np
 import pytest
 
@@ -17,7 +19,8 @@ from tests.gpu_util import dev, host, log
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("branched", [False, True])
+def test_graph_replay_matches_eager(branched):
     import torch
 
     import quantized_diffusion_transformer_qlinear_amd as q
@@ -36,10 +39,20 @@ def test_graph_replay_matches_eager():
     y2 = torch.empty((M, si.MLP), dtype=torch.float16, device="cuda:0")
     y4 = torch.empty((16, si.MLP), dtype=torch.float16, device="cuda:0")
 
-    def step():
-        chain.run(h)
+    side = torch.cuda.Stream()
+
+    def step(fork=False):
+        cur = torch.cuda.current_stream()
+        if fork:
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                chain.run(h)
+        else:
+            chain.run(h)
         q.qlinear_w8a16(x2, wq2, sw2, y=y2, bias=b2, gelu=True)
         q.qlinear_w4a16(x4, wq4, sg4, y=y4)
+        if fork:
+            cur.wait_stream(side)
 
     def outputs():
         return host(chain.out).tobytes(), host(y2).tobytes(), host(y4).tobytes()
@@ -56,13 +69,13 @@ def test_graph_replay_matches_eager():
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g, stream=cap):
-            step()
+            step(fork=branched)
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
 
     other = dev(np.random.default_rng(0).standard_normal((64, si.WIDTH)).astype(np.float16))
     for rep in range(4):
-        log(f"replay {rep}")
+        log(f"replay {rep} (branched {branched})")
         for buf in (chain.out, y2, y4):
             buf.fill_(0)
         q.qlinear_w8a16(other, wq2, sw2)   # unrelated eager work between replays
