@@ -158,9 +158,11 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
     """W4A16 at small M, where the layer is bound by streaming its 4-bit weights:
     the same 1536x6144 layer as `copies` distinct packed copies (1.06 GB, past
     the 256 MB last-level cache, so every launch reads its weights from HBM),
-    timed three ways: (1) one launch after the other copies ran (cold), (2) a
-    graph of dependent single launches over the copies, (3) the grouped call
-    over the copies (16 layers per launch) in a graph."""
+    timed four ways: (1) one launch after the other copies ran (cold), (2) a
+    graph of dependent single launches over the copies, (3) the same single
+    launches as independent graph nodes, four parallel branches (copy j on
+    branch j % 4), (4) the grouped call over the copies (16 layers per
+    launch) in a graph."""
     K, N = w.shape
     wd = torch.from_numpy(w).to(dev)
     wq, sg = q.qpack(4, wd)
@@ -193,6 +195,22 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
         for j in range(copies):
             q.qlinear_w4a16(x, cps[j][0], cps[j][1], y=ys[j])
 
+    side = [torch.cuda.Stream() for _ in range(3)]
+
+    def run_branched():
+        cur = torch.cuda.current_stream()
+        for st in side:
+            st.wait_stream(cur)
+        for j in range(copies):
+            b = j % 4
+            if b == 0:
+                q.qlinear_w4a16(x, cps[j][0], cps[j][1], y=ys[j])
+            else:
+                with torch.cuda.stream(side[b - 1]):
+                    q.qlinear_w4a16(x, cps[j][0], cps[j][1], y=ys[j])
+        for st in side:
+            cur.wait_stream(st)
+
     cold = []
     for _ in range(5):
         run_all()
@@ -206,6 +224,7 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
     probs = [{"x": x, "wq": cps[j][0], "s": cps[j][1], "y": ys[j]} for j in range(copies)]
     out = {}
     for name, g in (("graph_of_single_launches", graph_of(run_all)),
+                    ("graph_of_independent_launches", graph_of(run_branched)),
                     ("grouped", graph_of(lambda: q.qlinear_grouped(4, probs)))):
         ts = []
         for _ in range(5):
@@ -218,8 +237,10 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
         out[name] = med(ts)
     res = {"M": M, "K": K, "N": N, "bytes_per_layer": layer_bytes, "copies": copies,
            "reading": "the 70% HBM target is read against 'graph_of_single_launches' (dependent launches); "
+                      "'graph_of_independent_launches' runs the same launches as concurrent graph nodes; "
                       "'grouped' is the one-launch-per-16-layers streaming path"}
     for name, us in (("single_cold", med(cold)), ("graph_of_single_launches", out["graph_of_single_launches"]),
+                     ("graph_of_independent_launches", out["graph_of_independent_launches"]),
                      ("grouped", out["grouped"])):
         gbs = layer_bytes / us / 1e3
         res[name] = {"us_per_layer": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK["hbm"], 4)}
