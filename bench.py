@@ -320,7 +320,7 @@ def full_block(q, torch, dev, si, blk, packed, reps=20):
             "tops_incl_attention": round((lin_ops + attn_flops) / us_graph / 1e6, 1)}
 
 
-def step_1p2b(q, torch, dev, si, reps=5):
+def step_1p2b(q, torch, dev, si, reps=5, nbr=2):
     """The 1.2B-parameter-scale denoising step: 24 blocks x {QKV 2048->6144,
     out 2048->2048, MLP-up 2048->8192, MLP-down 8192->2048} = 1,207,959,552
     linear weights, every linear over the same M = 2048 tokens with a plain
@@ -328,8 +328,8 @@ def step_1p2b(q, torch, dev, si, reps=5):
     Weights are seeded N(0, 0.02) drawn on the device and packed at 8 and at 4
     bits (the fp16 copy is released after packing); the step runs at q8
     (W8A16), q4 (W4A16) and W8A8 on the q8 storage.  Each precision's 96 calls
-    are captured as one graph, in two parallel branches (linear i on branch
-    i % 2, each branch with its own outputs and workspace; also timed on one
+    are captured as one graph, in `nbr` parallel branches (linear i on branch
+    i % nbr, each branch with its own outputs and workspace; also timed on one
     stream as `serial_ms_per_step`), and replayed: ms per step, aggregate TOPS,
     algorithmic bytes / time (packed weights + scales + X + Y per linear) and
     the resident packed footprint (measured allocation and the packed sizes)."""
@@ -353,7 +353,6 @@ def step_1p2b(q, torch, dev, si, reps=5):
     gen.manual_seed(501)
     xs = {K: torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32).half()
           for K in sorted({K for _n, K, _N in si.STEP_LAYERS})}
-    nbr = 2
     ys = [{N: torch.empty((M, N), dtype=torch.float16, device=dev) for N in sorted({N for _n, _K, N in si.STEP_LAYERS})}
           for _ in range(nbr)]
     wsb = max(max(q.workspace_bytes(q.ARIA_W8A8, M, K, N) for _n, K, N in si.STEP_LAYERS), 1)
