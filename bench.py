@@ -483,7 +483,7 @@ def main():
     x3d = up(x3)
     y3 = torch.empty((M, si.MLP), dtype=torch.float16, device=dev)
 
-    names = ["w8a8.qkv", "attention(copy)", "w8a8.out", "w8a8.up", "w8a8.down", "w8a16.up", "w4a16"]
+    names = ["w8a8.qkv", "w8a8.out", "w8a8.up", "w8a8.down", "w8a16.up", "w4a16"]
 
     # The step's three groups are independent: the W8A8 chain, the W8A16
     # layer and the W4A16 layer.  Replayed as a graph they run as parallel
@@ -544,7 +544,7 @@ def main():
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
     # per-call durations: each call alone, graph-replayed on its own stream
-    call_fns = dict(zip(["w8a8.qkv", "attention(copy)", "w8a8.out", "w8a8.up", "w8a8.down"],
+    call_fns = dict(zip(["w8a8.qkv", "w8a8.out", "w8a8.up", "w8a8.down"],
                         [fn for _n, fn in chain.calls(h)]))
     call_fns["w8a16.up"] = lambda: q.qlinear_w8a16(x2, wq2, sw2, y=y2, bias=b2, gelu=True)
     call_fns["w4a16"] = lambda: q.qlinear_w4a16(x3d, wq3, sg3, y=y3)
@@ -575,11 +575,10 @@ def main():
         calls[n] = {"us": round(per[n], 2), "tops": round(2.0 * M * K * N / per[n] / 1e6, 1),
                     "bound": rf["bound"], "frac": round(rf["frac"], 4),
                     "launches": 2 if mode == "w8a8" else 1}
-    calls["attention(copy)"] = {"us": round(per["attention(copy)"], 2)}
     modes = {}
     for mode, members in (("w8a8_chain", [n for n in lin if n.startswith("w8a8")]), ("w8a16", ["w8a16.up"]),
                           ("w4a16", ["w4a16"])):
-        us = sum(per[n] for n in members) + (per["attention(copy)"] if mode == "w8a8_chain" else 0.0)
+        us = sum(per[n] for n in members)
         ops = sum(2.0 * M * lin[n][1] * lin[n][2] for n in members)
         modes[mode] = {"us": round(us, 2), "tops": round(ops / us / 1e6, 1)}
 

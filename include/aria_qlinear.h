@@ -105,6 +105,14 @@ int aria_qpack(int bits, int group, const void* w_f16, int64_t K, int64_t N,
 int aria_quant_act(const void* x_f16, int64_t M, int64_t K, int8_t* xq, void* s_a_f16,
                    aria_stream_t stream);
 
+/* a2 with a row stride: row m of X is the K halves at x + m * ldx (ldx >= K,
+ * ldx % 8 == 0), e.g. a column block of a wider activation such as the V third
+ * of a QKV output, quantized in place without a copy; Xq int8 [M][K] and
+ * s_a fp16 [M] are contiguous and identical to aria_quant_act on the gathered
+ * rows.  Feed them to aria_qlinear_w8a8_prequant. */
+int aria_quant_act_strided(const void* x_f16, int64_t ldx, int64_t M, int64_t K, int8_t* xq,
+                           void* s_a_f16, aria_stream_t stream);
+
 /* a5 — epilogue applied to every output element y[m][n] (in fp32, then
  * rounded to fp16 once): dequantize, then each optional term in this order. */
 typedef struct aria_epilogue {

@@ -11,5 +11,5 @@ the binding without the built library raises.
 from .binding import (  # noqa: F401
     ARIA_W4A16, ARIA_W8A16, ARIA_W8A8, ARIA_W16A16, AriaError, attention, layernorm, layernorm_quant, lib,
     library_path, qlinear_grouped, qlinear_w4a16, qlinear_w8a8, qlinear_w8a8_prequant, qlinear_w8a16,
-    qlinear_w16a16, qpack, qpack_bytes, quant_act, status_string, workspace_bytes,
+    qlinear_w16a16, qpack, qpack_bytes, quant_act, quant_act_columns, status_string, workspace_bytes,
 )

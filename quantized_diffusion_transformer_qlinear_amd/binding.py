@@ -34,6 +34,8 @@ lib.aria_qpack.argtypes = [_I, _I, _P, _I64, _I64, _P, _P, _P]
 lib.aria_qpack.restype = _I
 lib.aria_quant_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
 lib.aria_quant_act.restype = _I
+lib.aria_quant_act_strided.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
+lib.aria_quant_act_strided.restype = _I
 lib.aria_qlinear_workspace_bytes.argtypes = [_I, _I64, _I64, _I64]
 lib.aria_qlinear_workspace_bytes.restype = _SZ
 for _name in ("aria_qlinear_w8a8", "aria_qlinear_w8a16"):
@@ -136,6 +138,21 @@ def quant_act(x, xq=None, sa=None, stream=None):
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device) if xq is None else xq
     sa = torch.empty((M,), dtype=torch.float16, device=x.device) if sa is None else sa
     _check(lib.aria_quant_act(_addr(x), M, K, _addr(xq), _addr(sa), _stream(stream)), "quant_act")
+    return xq, sa
+
+
+def quant_act_columns(src, col0: int, ncols: int, xq=None, sa=None, stream=None):
+    """Per-token quantization of the column block src[:, col0:col0+ncols] of a
+    contiguous fp16 [M][W] tensor, read in place (row stride W)."""
+    torch = _torch()
+    _dt(src, torch.float16, "src")
+    M, W = src.shape
+    if not (0 <= col0 and col0 + ncols <= W):
+        raise ValueError("column block outside the tensor")
+    xq = torch.empty((M, ncols), dtype=torch.int8, device=src.device) if xq is None else xq
+    sa = torch.empty((M,), dtype=torch.float16, device=src.device) if sa is None else sa
+    _check(lib.aria_quant_act_strided(_addr(src) + 2 * col0, W, M, ncols, _addr(xq), _addr(sa), _stream(stream)),
+           "quant_act_strided")
     return xq, sa
 
 

@@ -8,30 +8,13 @@ QKV -> attention -> out-projection (+ residual) -> MLP-up (GELU) -> MLP-down
 (+ residual + alpha * d).  The attention core is not a quantized linear; it is
 stood in for by identity attention (each token attends only to itself, so the
 attention output is the V third of the QKV output), which keeps the chain
-data-dependent and row-local.  The stand-in is a strided device-to-device copy
-(hipMemcpy2DAsync); every arithmetic step runs in the qlinear kernels.
+data-dependent and row-local.  The out-projection's per-token quantization
+reads that third in place (a row-strided act-quant), so the stand-in costs no
+copy; every arithmetic step runs in the qlinear kernels.
 """
 from __future__ import annotations
 
-import ctypes
-
 from . import binding as B
-
-_hip = ctypes.CDLL("libamdhip64.so")
-_hip.hipMemcpy2DAsync.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
-                                  ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
-_hip.hipMemcpy2DAsync.restype = ctypes.c_int
-_D2D = 3  # hipMemcpyDeviceToDevice
-
-
-def copy_columns(dst, src, col0: int, ncols: int, stream=None):
-    """dst[:, :] = src[:, col0:col0+ncols] for fp16 row-major tensors (device copy)."""
-    M = src.shape[0]
-    es = src.element_size()
-    rc = _hip.hipMemcpy2DAsync(dst.data_ptr(), dst.shape[1] * es, src.data_ptr() + col0 * es, src.shape[1] * es,
-                               ncols * es, M, _D2D, B._stream(stream))
-    if rc != 0:
-        raise RuntimeError(f"hipMemcpy2DAsync failed ({rc})")
 
 
 class DitBlockW8A8:
@@ -45,7 +28,8 @@ class DitBlockW8A8:
         self.steer_dir, self.steer_alpha = steer_dir, steer_alpha
         f16 = torch.float16
         self.qkv = torch.empty((M, 3 * width), dtype=f16, device=dev)
-        self.a = torch.empty((M, width), dtype=f16, device=dev)
+        self.xq = torch.empty((M, width), dtype=torch.int8, device=dev)   # quantized V third
+        self.sa = torch.empty((M,), dtype=f16, device=dev)
         self.h1 = torch.empty((M, width), dtype=f16, device=dev)
         self.u = torch.empty((M, mlp), dtype=f16, device=dev)
         self.out = torch.empty((M, width), dtype=f16, device=dev)
@@ -53,15 +37,20 @@ class DitBlockW8A8:
                    for k, n in ((width, 3 * width), (width, width), (width, mlp), (mlp, width)))
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
+    def _out(self, h, stream):
+        # identity attention: the out-projection's input is the V third of qkv
+        B.quant_act_columns(self.qkv, 2 * self.width, self.width, xq=self.xq, sa=self.sa, stream=stream)
+        B.qlinear_w8a8_prequant(self.xq, self.sa, *self.packed["o"], y=self.h1, residual=h, stream=stream)
+
     def calls(self, h, stream=None):
         """The stages as (name, callable) pairs, in order; each call enqueues one
         stage on the stream (re-running one alone recomputes it from the
-        buffers the previous stage left)."""
+        buffers the previous stage left).  Each linear's stage includes its
+        activation quantization."""
         p = self.packed
         return [
             ("qkv", lambda: B.qlinear_w8a8(h, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)),
-            ("attention", lambda: copy_columns(self.a, self.qkv, 2 * self.width, self.width, stream)),
-            ("out", lambda: B.qlinear_w8a8(self.a, *p["o"], y=self.h1, ws=self.ws, residual=h, stream=stream)),
+            ("out", lambda: self._out(h, stream)),
             ("up", lambda: B.qlinear_w8a8(self.h1, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)),
             ("down", lambda: B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,
                                             steer_dir=self.steer_dir, steer_alpha=self.steer_alpha,

@@ -19,14 +19,14 @@
 namespace aria {
 
 template <int CH>  // CH 16-byte chunks per lane kept in registers (K <= CH * 512)
-__global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict__ x, int M, int K,
+__global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict__ x, int64_t ldx, int M, int K,
                                                        int8_t* __restrict__ xq, half_t* __restrict__ sa) {
     const int lane = threadIdx.x % WAVE;
     // the row is uniform over the wave; saying so keeps the buffer descriptors
     // in scalar registers (no per-lane waterfall around each load)
     const int m = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE);
     if (m >= M) return;
-    const rsrc_t rx = make_rsrc(x + (int64_t)m * K, (uint32_t)K * 2);
+    const rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, (uint32_t)K * 2);   // row m: K halves at stride ldx
     const rsrc_t rq = make_rsrc(xq + (int64_t)m * K, (uint32_t)K);
     v8h v[CH];
 #pragma unroll
@@ -34,20 +34,22 @@ __global__ __launch_bounds__(256) void actquant_kernel(const half_t* __restrict_
     quantize_row<CH>(v, lane, m, rq, sa);
 }
 
-hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, half_t* sa, hipStream_t st) {
+hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, half_t* sa, hipStream_t st,
+                           int64_t ldx) {
+    if (ldx == 0) ldx = K;
     const int rows_per_block = 4;
     dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(rows_per_block * WAVE);
     const int64_t ch = (K + 511) / 512;
     const int m = (int)M, k = (int)K;
-    if (ch <= 1) hipLaunchKernelGGL(actquant_kernel<1>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 2) hipLaunchKernelGGL(actquant_kernel<2>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 3) hipLaunchKernelGGL(actquant_kernel<3>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 4) hipLaunchKernelGGL(actquant_kernel<4>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 6) hipLaunchKernelGGL(actquant_kernel<6>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 8) hipLaunchKernelGGL(actquant_kernel<8>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 12) hipLaunchKernelGGL(actquant_kernel<12>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 16) hipLaunchKernelGGL(actquant_kernel<16>, grid, block, 0, st, x, m, k, xq, sa);
-    else if (ch <= 32) hipLaunchKernelGGL(actquant_kernel<32>, grid, block, 0, st, x, m, k, xq, sa);
+    if (ch <= 1) hipLaunchKernelGGL(actquant_kernel<1>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 2) hipLaunchKernelGGL(actquant_kernel<2>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 3) hipLaunchKernelGGL(actquant_kernel<3>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 4) hipLaunchKernelGGL(actquant_kernel<4>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 6) hipLaunchKernelGGL(actquant_kernel<6>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 8) hipLaunchKernelGGL(actquant_kernel<8>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 12) hipLaunchKernelGGL(actquant_kernel<12>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 16) hipLaunchKernelGGL(actquant_kernel<16>, grid, block, 0, st, x, ldx, m, k, xq, sa);
+    else if (ch <= 32) hipLaunchKernelGGL(actquant_kernel<32>, grid, block, 0, st, x, ldx, m, k, xq, sa);
     else return hipErrorInvalidValue;  // K > 16384: rejected on the host before this point
     return hipGetLastError();
 }

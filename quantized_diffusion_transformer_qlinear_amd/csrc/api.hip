@@ -127,6 +127,21 @@ int aria_quant_act(const void* x, int64_t M, int64_t K, int8_t* xq, void* sa, ar
                                       static_cast<hipStream_t>(stream)));
 }
 
+int aria_quant_act_strided(const void* x, int64_t ldx, int64_t M, int64_t K, int8_t* xq, void* sa,
+                           aria_stream_t stream) {
+    if (check_shape(M, K, 1) != ARIA_OK || ldx < K || ldx % 8 != 0 || ldx > ((int64_t)1 << 40) / M)
+        return ARIA_E_SHAPE;
+    if (!x || !xq || !sa) return ARIA_E_NULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(sa)) return ARIA_E_ALIGN;
+    const size_t xb = (size_t)((M - 1) * ldx + K) * 2;   // first to last byte of the rows read
+    if (overlap(x, xb, xq, (size_t)(M * K)) || overlap(x, xb, sa, (size_t)M * 2) ||
+        overlap(xq, (size_t)(M * K), sa, (size_t)M * 2))
+        return ARIA_E_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(launch_actquant(static_cast<const half_t*>(x), M, K, xq, static_cast<half_t*>(sa),
+                                      static_cast<hipStream_t>(stream), ldx));
+}
+
 size_t aria_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, int64_t N) {
     if (check_shape(M, K, N) != ARIA_OK) return 0;
     switch (mode) {

@@ -7,7 +7,9 @@ namespace aria {
 
 hipError_t launch_qpack8(const half_t* w, int64_t K, int64_t N, int8_t* q, half_t* s, hipStream_t st);
 hipError_t launch_qpack4(const half_t* w, int64_t K, int64_t N, uint8_t* q4, half_t* s, hipStream_t st);
-hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, half_t* sa, hipStream_t st);
+// ldx: row stride of x in halves (0: K, rows contiguous)
+hipError_t launch_actquant(const half_t* x, int64_t M, int64_t K, int8_t* xq, half_t* sa, hipStream_t st,
+                           int64_t ldx = 0);
 hipError_t launch_pack16(const half_t* w, int64_t K, int64_t N, half_t* wt, hipStream_t st);
 
 // The DiT block's steps around the linears (layernorm.hip, attention.hip).

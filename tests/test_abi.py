@@ -29,7 +29,7 @@ def q():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (aria_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -105,6 +105,12 @@ def test_validation_codes(q):
     assert L.aria_qpack(8, 0, X, 64, 64, X + 64, S, None) == -7
     assert L.aria_quant_act(X, 64, 33, W, S, None) == -2
     assert L.aria_quant_act(X, 64, 64, None, S, None) == -1
+    assert L.aria_quant_act_strided(X, 32, 64, 64, W, S, None) == -2        # ldx < K
+    assert L.aria_quant_act_strided(X, 100, 64, 64, W, S, None) == -2       # ldx % 8
+    assert L.aria_quant_act_strided(X, 192, 64, 64, None, S, None) == -1
+    assert L.aria_quant_act_strided(X + 2, 192, 64, 64, W, S, None) == -3
+    assert L.aria_quant_act_strided(X, 192, 64, 64, X + 1024, S, None) == -7     # xq inside the rows read
+    assert L.aria_quant_act_strided(X, 192, 64, 64, W, W + 1024, None) == -7     # s_a inside xq
     # the fp16 rung
     assert L.aria_qlinear_w16a16(X, 64, 256, 256, None, None, Y, None, 0, None) == -1
     assert L.aria_qlinear_w16a16(X, 64, 48, 256, W, None, Y, None, 0, None) == -2

@@ -55,8 +55,8 @@ def test_chain_stagewise_bit_exact(setup):
     torch.cuda.synchronize()
     hh = blk["h"][rows]
     stages = [  # name, GPU stage input, oracle stage input, weights, epilogue (GPU buffers / oracle arrays)
-        ("qkv", chain.a.new_empty(0), None, "qkv", {}),
-        ("out", chain.a, ref["a"], "o", {"residual": (h, hh)}),
+        ("qkv", None, None, "qkv", {}),
+        ("out", None, ref["a"], "o", {"residual": (h, hh)}),   # identity attention: the V third of qkv
         ("up", chain.h1, ref["h1"], "up", {"gelu": True}),
         ("down", chain.u, ref["u"], "down", {"residual": (chain.h1, ref["h1"]), "d": True}),
     ]
@@ -65,7 +65,8 @@ def test_chain_stagewise_bit_exact(setup):
         if name == "qkv":
             x_host, oin = blk["h"].copy(), hh
         else:
-            x_host = host(gin).copy()
+            W = packed["o"][0].shape[1]
+            x_host = (host(chain.qkv)[:, 2 * W:] if name == "out" else host(gin)).copy()
             x_host[rows] = oin                    # the oracle's own stage input on the sampled rows
         x = dev(x_host)
         kw, okw = {}, {}

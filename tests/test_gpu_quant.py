@@ -122,3 +122,17 @@ def test_actquant_dit_shapes(q):
     x2 = si.normal_f16((2048, 6144), 1.0, 999)
     log("actquant 2048x6144")
     _actquant_both(q, x2)
+
+
+@pytest.mark.parametrize("M,W,col0,ncols", [(1, 96, 64, 32), (77, 4608, 3072, 1536), (2048, 4608, 3072, 1536),
+                                            (130, 1024, 8, 512)])
+def test_quant_act_columns(q, M, W, col0, ncols):
+    """The row-strided act-quant of a column block read in place equals the
+    oracle's quantization of that block, bit for bit."""
+    rng = np.random.default_rng(M + W + col0)
+    x = (rng.standard_normal((M, W)) * 3).astype(np.float16)
+    log(f"quant_act_columns M={M} W={W} cols {col0}+{ncols}")
+    xq, sa = q.quant_act_columns(dev(x), col0, ncols)
+    xq_ref, sa_ref = oracle.quant_act(np.ascontiguousarray(x[:, col0:col0 + ncols]))
+    assert np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(host(sa).view(np.uint16), sa_ref.view(np.uint16))
