@@ -1,9 +1,13 @@
 """Mutation check of the oracle's pins.
 
-Each case plants one plausible mistake in a private copy of the oracle's C
-source (on the CPU only), builds it, and runs the oracle pin suite against it
-in a subprocess: every mutant must make at least one pin fail.  The real oracle
-is never modified."""
+Each case plants one plausible mistake in a private copy of the oracle (on
+the CPU only) and runs the oracle pin suite against it in a subprocess: every
+mutant must make at least one pin fail.  C mutants edit the arithmetic in
+``aria_oracle.c`` and are built into their own library; Python mutants edit
+the block compositions in ``oracle/__init__.py`` (which third of QKV is V,
+which tensor each residual reads, where GELU and the steering term go, which
+input each norm reads) and run from a private copy of the tree.  The real
+oracle is never modified."""
 import os
 import shutil
 import subprocess
@@ -18,7 +22,9 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "aria_oracle.c")
 PIN_FILES = ["tests/test_oracle_codec.py", "tests/test_oracle_quant.py", "tests/test_oracle_pack.py",
-             "tests/test_oracle_gemm.py", "tests/test_oracle_epilogue.py", "tests/test_oracle_block.py"]
+             "tests/test_oracle_gemm.py", "tests/test_oracle_epilogue.py", "tests/test_oracle_block.py",
+             "tests/test_oracle_chain.py"]
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
 
 MUTANTS = {
     "rne_ties_up": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
@@ -56,6 +62,42 @@ MUTANTS = {
 }
 
 
+# Python mutants: name -> list of (old, new, occurrence) edits of oracle/__init__.py
+# (occurrence: which match of `old` to replace; the two block functions share
+# some lines).  The first two groups follow the identity-attention chain
+# (dit_block_w8a8), the last the full block (dit_block_full_w8a8).
+_DOWN = 'out64 = qlinear_w8a8(u, *packed["down"], residual=h1, d=d, alpha=alpha)["y"]'
+_OUT = 'h1 = f64_to_f16(qlinear_w8a8(a, *packed["o"], residual=h)["y"])'
+PY_MUTANTS = {
+    "chain_v_slice_k": [("qkv[:, 2 * width:3 * width]", "qkv[:, width:2 * width]", 0)],
+    "chain_v_slice_q": [("qkv[:, 2 * width:3 * width]", "qkv[:, 0:width]", 0)],
+    "chain_down_residual_h": [(_DOWN, _DOWN.replace("residual=h1", "residual=h"), 1)],
+    "chain_steer_on_out": [(_OUT, _OUT.replace("residual=h)", "residual=h, d=d, alpha=alpha)"), 1),
+                           (_DOWN, _DOWN.replace(", d=d, alpha=alpha", ""), 1)],
+    "chain_gelu_on_down": [('qlinear_w8a8(h1, *packed["up"], gelu=True)', 'qlinear_w8a8(h1, *packed["up"])', 0),
+                           (_DOWN, _DOWN.replace("residual=h1,", "residual=h1, gelu=True,"), 1)],
+    "chain_out_no_residual": [(_OUT, _OUT.replace(", residual=h", ""), 1)],
+    "chain_up_reads_h": [('qlinear_w8a8(h1, *packed["up"], gelu=True)', 'qlinear_w8a8(h, *packed["up"], gelu=True)', 0)],
+    "full_qkv_reads_h": [('qlinear_w8a8(n1, *packed["qkv"])', 'qlinear_w8a8(h, *packed["qkv"])', 0)],
+    "full_ln1_params": [("n1 = f64_to_f16(layernorm(h, *ln1, eps))", "n1 = f64_to_f16(layernorm(h, *ln2, eps))", 0)],
+    "full_ln2_reads_h": [("layernorm(h1, *ln2, eps)", "layernorm(h, *ln2, eps)", 0)],
+    "full_attention_one_sequence": [("attention(qkv, heads, seq)", "attention(qkv, heads, qkv.shape[0])", 0)],
+    "full_out_residual_n1": [(_OUT, _OUT.replace("residual=h)", "residual=n1)"), 0)],
+    "full_down_residual_h": [(_DOWN, _DOWN.replace("residual=h1", "residual=h"), 0)],
+    "full_steer_on_out": [(_OUT, _OUT.replace("residual=h)", "residual=h, d=d, alpha=alpha)"), 0),
+                          (_DOWN, _DOWN.replace(", d=d, alpha=alpha", ""), 0)],
+    "full_gelu_on_down": [('qlinear_w8a8(n2, *packed["up"], gelu=True)', 'qlinear_w8a8(n2, *packed["up"])', 0),
+                          (_DOWN, _DOWN.replace("residual=h1,", "residual=h1, gelu=True,"), 0)],
+}
+
+
+def _pytest(cwd, env):
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-W", "ignore::RuntimeWarning", *PIN_FILES],
+                       cwd=cwd, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode
+
+
 def _run_mutant(name, tmp):
     old, new = MUTANTS[name]
     src = open(SRC).read()
@@ -67,17 +109,41 @@ def _run_mutant(name, tmp):
     open(c, "w").write(src.replace(old, new))
     subprocess.run(["gcc", *oracle._CFLAGS, "-w", c, "-o", so, "-lm"], check=True)
     env = dict(os.environ, ARIA_ORACLE_LIB=so, OMP_NUM_THREADS="1")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "-W", "ignore::RuntimeWarning", *PIN_FILES],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    return name, r.returncode
+    return name, _pytest(ROOT, env)
+
+
+def _replace_nth(src, old, new, n):
+    at = -1
+    for _ in range(n + 1):
+        at = src.find(old, at + 1)
+        assert at >= 0, f"mutation site {old!r} has no occurrence {n}"
+    return src[:at] + new + src[at + len(old):]
+
+
+def _run_py_mutant(name, tmp):
+    """Copy the tests, the input generators and the oracle package into a
+    private tree, edit the copy's __init__.py, run the pins there (their
+    conftest puts that tree first on sys.path) against the real C library."""
+    d = os.path.join(tmp, name)
+    shutil.copytree(os.path.join(ROOT, "tests"), os.path.join(d, "tests"),
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copy(os.path.join(ROOT, "synthetic_inputs.py"), d)
+    os.makedirs(os.path.join(d, "oracle"))
+    src = open(PY_SRC).read()
+    for old, new, n in PY_MUTANTS[name]:
+        src = _replace_nth(src, old, new, n)
+    open(os.path.join(d, "oracle", "__init__.py"), "w").write(src)
+    env = dict(os.environ, ARIA_ORACLE_LIB=oracle.build(force=False), OMP_NUM_THREADS="1")
+    return name, _pytest(d, env)
 
 
 def test_every_mutant_is_caught():
     tmp = tempfile.mkdtemp(prefix="oracle_mutants_")
     try:
         with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-            results = dict(ex.map(lambda n: _run_mutant(n, tmp), MUTANTS))
+            jobs = [ex.submit(_run_mutant, n, tmp) for n in MUTANTS]
+            jobs += [ex.submit(_run_py_mutant, n, tmp) for n in PY_MUTANTS]
+            results = dict(j.result() for j in jobs)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     survivors = [n for n, rc in results.items() if rc == 0]
@@ -95,5 +161,18 @@ def test_unmutated_copy_passes():
         name, rc = _run_mutant("_control", tmp)
     finally:
         MUTANTS.pop("_control", None)
+        shutil.rmtree(tmp, ignore_errors=True)
+    assert rc == 0
+
+
+def test_unmutated_python_copy_passes():
+    """Control for the Python mutants: the private tree with an unedited
+    __init__.py passes."""
+    tmp = tempfile.mkdtemp(prefix="oracle_control_py_")
+    try:
+        PY_MUTANTS["_control"] = []
+        name, rc = _run_py_mutant("_control", tmp)
+    finally:
+        PY_MUTANTS.pop("_control", None)
         shutil.rmtree(tmp, ignore_errors=True)
     assert rc == 0
