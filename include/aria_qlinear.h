@@ -130,7 +130,8 @@ typedef struct aria_epilogue {
 /* Workspace (device bytes) the qlinear call needs for this shape; 0 = none.
  * W8A8 needs room for Xq int8 [M][K] and s_a fp16 [M] (256-byte aligned
  * parts); the weight-only modes currently need none, but callers should query
- * rather than assume.
+ * rather than assume.  A workspace may not overlap any other buffer of the
+ * call (ARIA_E_ALIAS), and neither may the raw accumulators acc_out.
  *
  * Tile choice (M > 64) is automatic; the environment variable
  * ARIA_QLINEAR_TILE="BMxBNxWMxWN[xKS]" forces one of the library's tile

@@ -46,6 +46,13 @@ int make_epi(const aria_epilogue* e, int mode, int64_t M, int64_t N, const void*
     // the residual may be exactly y (in-place h += ...), but must not partly overlap it
     const size_t ybytes = (size_t)(M * N) * 2;
     if (e->residual && e->residual != y && overlap(e->residual, ybytes, y, ybytes)) return ARIA_E_ALIAS;
+    // the raw accumulators are an output of their own
+    const size_t abytes = (size_t)(M * N) * 4;
+    if (e->acc_out && (overlap(e->acc_out, abytes, y, ybytes) || (e->residual && overlap(e->acc_out, abytes, e->residual, ybytes)) ||
+                       (e->bias && overlap(e->acc_out, abytes, e->bias, (size_t)N * 2)) ||
+                       (e->steer_dir && overlap(e->acc_out, abytes, e->steer_dir, (size_t)N * 4)) ||
+                       (e->steer_alpha && overlap(e->acc_out, abytes, e->steer_alpha, 4))))
+        return ARIA_E_ALIAS;
     out->bias = static_cast<const half_t*>(e->bias);
     out->residual = static_cast<const half_t*>(e->residual);
     out->steer_dir = e->steer_dir;
@@ -56,6 +63,16 @@ int make_epi(const aria_epilogue* e, int mode, int64_t M, int64_t N, const void*
 }
 
 size_t w8a8_ws(int64_t M, int64_t K) { return round_up((size_t)(M * K), kAlign) + round_up((size_t)M * 2, kAlign); }
+
+// Does any buffer of the epilogue overlap [p, p + n)?  (The residual is
+// checked against y by make_epi; here it is one more buffer.)
+bool epi_overlaps(const aria_epilogue* e, int64_t M, int64_t N, const void* p, size_t n) {
+    if (!e) return false;
+    const size_t mn = (size_t)(M * N);
+    return (e->bias && overlap(e->bias, (size_t)N * 2, p, n)) || (e->residual && overlap(e->residual, mn * 2, p, n)) ||
+           (e->steer_dir && overlap(e->steer_dir, (size_t)N * 4, p, n)) ||
+           (e->steer_alpha && overlap(e->steer_alpha, 4, p, n)) || (e->acc_out && overlap(e->acc_out, mn * 4, p, n));
+}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ARIA_OK : ARIA_E_HIP; }
 
@@ -153,24 +170,53 @@ size_t aria_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, int64_t N) {
     }
 }
 
-int aria_qlinear_w8a8(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
-                      const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The W8A8 checks apart from those of the workspace.
+int w8a8_check(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
+               const aria_epilogue* epi, void* y, Epi* e) {
     int rc = check_shape(M, K, N);
     if (rc != ARIA_OK) return rc;
     if (!x || !wq || !sw || !y) return ARIA_E_NULL;
-    if (!aligned16(x) || !aligned16(wq) || !aligned16(sw) || !aligned16(y) || !aligned16(ws)) return ARIA_E_ALIGN;
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(sw) || !aligned16(y)) return ARIA_E_ALIGN;
     if (overlap(x, (size_t)(M * K) * 2, y, (size_t)(M * N) * 2)) return ARIA_E_ALIAS;
-    Epi e;
-    if ((rc = make_epi(epi, ARIA_W8A8, M, N, y, &e)) != ARIA_OK) return rc;
-    const size_t need = w8a8_ws(M, K);
-    if (!ws || ws_bytes < need) return ARIA_E_WORKSPACE;
+    return make_epi(epi, ARIA_W8A8, M, N, y, e);
+}
+
+// act-quant of X into the workspace (Xq int8 [M][K], then s_a fp16 [M] at the
+// next 256-byte boundary), then the GEMM + epilogue reading it.
+int w8a8_launch(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw, const Epi& e,
+                void* y, void* ws, hipStream_t st) {
     int8_t* xq = static_cast<int8_t*>(ws);
     half_t* sa = reinterpret_cast<half_t*>(static_cast<char*>(ws) + round_up((size_t)(M * K), kAlign));
-    hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if ((rc = hip_status(launch_actquant(static_cast<const half_t*>(x), M, K, xq, sa, st))) != ARIA_OK) return rc;
+    int rc = hip_status(launch_actquant(static_cast<const half_t*>(x), M, K, xq, sa, st));
+    if (rc != ARIA_OK) return rc;
     return hip_status(launch_gemm_tiled(0, xq, wq, static_cast<const half_t*>(sw), sa, static_cast<half_t*>(y),
                                         (int)M, (int)N, (int)K, e, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int aria_qlinear_w8a8(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
+                      const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes, aria_stream_t stream) {
+    Epi e;
+    int rc = w8a8_check(x, M, K, N, wq, sw, epi, y, &e);
+    if (rc != ARIA_OK) return rc;
+    if (!aligned16(ws)) return ARIA_E_ALIGN;
+    const size_t need = w8a8_ws(M, K);
+    if (!ws || ws_bytes < need) return ARIA_E_WORKSPACE;
+    // the workspace is written while x, the weights and the epilogue
+    // operands are read, and y is written
+    if (overlap(ws, need, x, (size_t)(M * K) * 2) || overlap(ws, need, y, (size_t)(M * N) * 2) ||
+        overlap(ws, need, wq, (size_t)(N * K)) || overlap(ws, need, sw, (size_t)N * 2) ||
+        epi_overlaps(epi, M, N, ws, need))
+        return ARIA_E_ALIAS;
+    return w8a8_launch(x, M, K, N, wq, sw, e, y, ws, static_cast<hipStream_t>(stream));
 }
 
 static int wxa16(int bits, const void* x, int64_t M, int64_t K, int64_t N, const void* wq, const void* s,
@@ -186,6 +232,13 @@ static int wxa16(int bits, const void* x, int64_t M, int64_t K, int64_t N, const
     if ((rc = make_epi(epi, mode, M, N, y, &e)) != ARIA_OK) return rc;
     const size_t need = wxa16_workspace_bytes(bits, M, K, N);
     if (need && (!ws || ws_bytes < need)) return ARIA_E_WORKSPACE;
+    if (need) {
+        const size_t wb = bits == 8 ? (size_t)(N * K) : bits == 4 ? (size_t)(N * K) / 2 : (size_t)(N * K) * 2;
+        const size_t sb = bits == 8 ? (size_t)N * 2 : bits == 4 ? (size_t)N * (size_t)(K / 32) * 2 : 0;
+        if (overlap(ws, need, x, (size_t)(M * K) * 2) || overlap(ws, need, y, (size_t)(M * N) * 2) ||
+            overlap(ws, need, wq, wb) || (sb && overlap(ws, need, s, sb)) || epi_overlaps(epi, M, N, ws, need))
+            return ARIA_E_ALIAS;
+    }
     (void)hipGetLastError();
     return hip_status(launch_gemm_wxa16(bits, static_cast<const half_t*>(x), wq, static_cast<const half_t*>(s),
                                         static_cast<half_t*>(y), (int)M, (int)N, (int)K, e, ws, ws_bytes,

@@ -93,6 +93,22 @@ def test_validation_codes(q):
     assert _w8a8(q, X, 64, 256, 256, W, S, E(S + 2, 0, 0, None, None, None, None), Y, WS, big) == -3
     # residual partly overlapping y is rejected, exact aliasing is allowed past validation
     assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, Y + 512, None, None, None), Y, WS, big) == -7
+    # the workspace is written while x, the weights and the epilogue operands
+    # are read and y is written: it may overlap none of them
+    assert _w8a8(q, X, 64, 256, 256, W, S, None, Y, X + 4096, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, None, Y, Y + 4096, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, None, Y, W + 4096, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, None, Y, S - 256, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(WS + 1024, 0, 0, None, None, None, None), Y, WS, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, WS + 1024, None, None, None), Y, WS, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, None, 7 << 20, WS + 64, None), Y, WS, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, None, None, None, WS + 4096), Y, WS, big) == -7
+    # the raw accumulators may overlap neither y nor another epilogue operand
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, None, None, None, Y + 256), Y, WS, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(None, 0, 0, 9 << 20, None, None, (9 << 20) + 1024), Y, WS, big) == -7
+    assert _w8a8(q, X, 64, 256, 256, W, S, E(9 << 20, 0, 0, None, None, None, (9 << 20) - 256), Y, WS, big) == -7
+    assert L.aria_qlinear_w8a8_prequant(1 << 24, 2 << 24, 64, 256, 256, W, S,
+                                        ctypes.byref(E(None, 0, 0, None, None, None, Y + 1024)), Y, None) == -7
     # acc_out only for W8A8; group must be 32 for W4A16
     ep = E(None, 0, 0, None, None, None, 6 << 20)
     assert L.aria_qlinear_w8a16(X, 64, 256, 256, W, S, ctypes.byref(ep), Y, None, 0, None) == -4
