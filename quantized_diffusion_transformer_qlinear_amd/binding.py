@@ -1,6 +1,10 @@
 """ctypes binding of the C-ABI in include/aria_qlinear.h (same names, minus
-the ``aria_`` prefix).  Arguments are torch tensors on the GPU (or raw device
-addresses as ints); nothing here computes any part of the layer."""
+the ``aria_`` prefix).  Arguments are contiguous torch tensors on one GPU;
+nothing here computes any part of the layer.  The C-ABI receives raw pointers
+and cannot tell a buffer's size, so every wrapper checks each tensor's
+dtype, shape and device against the call's M, K, N before anything reaches
+the library (TypeError for a wrong dtype, ValueError for a wrong shape or
+device)."""
 from __future__ import annotations
 
 import ctypes
@@ -87,11 +91,9 @@ def _torch():
 
 
 def _addr(t):
-    """Device address of a tensor (None -> NULL); ints pass through."""
+    """Device address of a checked tensor (None -> NULL)."""
     if t is None:
         return None
-    if isinstance(t, int):
-        return t
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("expected a contiguous GPU tensor")
     return t.data_ptr()
@@ -103,9 +105,33 @@ def _stream(stream):
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
-def _dt(t, dtype, name):
-    if t is not None and not isinstance(t, int) and t.dtype != dtype:
+def _arg(t, dtype, shape, name, device=None):
+    """Check an operand: a torch tensor (or None) of `dtype`, exactly `shape`,
+    on `device` when given.  Returns t."""
+    if t is None:
+        return t
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the other operands on {device}")
+    return t
+
+
+def _mat(t, dtype, name):
+    """A 2-D operand whose shape defines the call: returns (rows, cols)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D tensor, got shape {tuple(t.shape)}")
+    return t.shape
 
 
 def qpack_bytes(bits: int, group: int, K: int, N: int):
@@ -118,25 +144,29 @@ def qpack(bits: int, w, q=None, s=None, stream=None):
     """Pack fp16 W [K][N]: bits 8 -> (Wq int8 [N][K], s fp16 [N]);
     bits 4 -> (Wq4 uint8 [N][K/2], s fp16 [N][K/32]); bits 16 -> (Wt fp16 [N][K], None)."""
     torch = _torch()
-    _dt(w, torch.float16, "w")
-    K, N = w.shape
+    if bits not in (4, 8, 16):
+        raise ValueError(f"bits must be 4, 8 or 16, got {bits}")
+    K, N = _mat(w, torch.float16, "w")
     group = 32 if bits == 4 else 0
-    if q is None:
-        shape = (N, K // 2) if bits == 4 else (N, K)
-        dtype = {8: torch.int8, 4: torch.uint8, 16: torch.float16}[bits]
-        q = torch.empty(shape, dtype=dtype, device=w.device)
-    if s is None and bits != 16:
-        s = torch.empty((N,) if bits == 8 else (N, K // group), dtype=torch.float16, device=w.device)
+    qshape = (N, K // 2) if bits == 4 else (N, K)
+    qtype = {8: torch.int8, 4: torch.uint8, 16: torch.float16}[bits]
+    sshape = (N,) if bits == 8 else (N, K // 32)
+    q = torch.empty(qshape, dtype=qtype, device=w.device) if q is None else _arg(q, qtype, qshape, "q", w.device)
+    if bits == 16:
+        s = None
+    else:
+        s = (torch.empty(sshape, dtype=torch.float16, device=w.device) if s is None
+             else _arg(s, torch.float16, sshape, "s", w.device))
     _check(lib.aria_qpack(bits, group, _addr(w), K, N, _addr(q), _addr(s), _stream(stream)), "qpack")
     return q, s
 
 
 def quant_act(x, xq=None, sa=None, stream=None):
     torch = _torch()
-    _dt(x, torch.float16, "x")
-    M, K = x.shape
+    M, K = _mat(x, torch.float16, "x")
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device) if xq is None else xq
     sa = torch.empty((M,), dtype=torch.float16, device=x.device) if sa is None else sa
+    _arg(xq, torch.int8, (M, K), "xq", x.device), _arg(sa, torch.float16, (M,), "sa", x.device)
     _check(lib.aria_quant_act(_addr(x), M, K, _addr(xq), _addr(sa), _stream(stream)), "quant_act")
     return xq, sa
 
@@ -145,12 +175,12 @@ def quant_act_columns(src, col0: int, ncols: int, xq=None, sa=None, stream=None)
     """Per-token quantization of the column block src[:, col0:col0+ncols] of a
     contiguous fp16 [M][W] tensor, read in place (row stride W)."""
     torch = _torch()
-    _dt(src, torch.float16, "src")
-    M, W = src.shape
-    if not (0 <= col0 and col0 + ncols <= W):
+    M, W = _mat(src, torch.float16, "src")
+    if not (0 <= col0 and 0 < ncols and col0 + ncols <= W):
         raise ValueError("column block outside the tensor")
     xq = torch.empty((M, ncols), dtype=torch.int8, device=src.device) if xq is None else xq
     sa = torch.empty((M,), dtype=torch.float16, device=src.device) if sa is None else sa
+    _arg(xq, torch.int8, (M, ncols), "xq", src.device), _arg(sa, torch.float16, (M,), "sa", src.device)
     _check(lib.aria_quant_act_strided(_addr(src) + 2 * col0, W, M, ncols, _addr(xq), _addr(sa), _stream(stream)),
            "quant_act_strided")
     return xq, sa
@@ -160,84 +190,94 @@ def workspace_bytes(mode: int, M: int, K: int, N: int) -> int:
     return int(lib.aria_qlinear_workspace_bytes(mode, M, K, N))
 
 
-def _epi(bias, gelu, residual, steer_dir, steer_alpha, acc_out):
+def _epi(M, N, device, bias, gelu, residual, steer_dir, steer_alpha, acc_out):
     torch = _torch()
-    _dt(bias, torch.float16, "bias")
-    _dt(residual, torch.float16, "residual")
-    _dt(steer_dir, torch.float32, "steer_dir")
-    _dt(steer_alpha, torch.float32, "steer_alpha")
-    _dt(acc_out, torch.int32, "acc_out")
+    _arg(bias, torch.float16, (N,), "bias", device)
+    _arg(residual, torch.float16, (M, N), "residual", device)
+    _arg(steer_dir, torch.float32, (N,), "steer_dir", device)
+    if steer_alpha is not None:
+        if not isinstance(steer_alpha, torch.Tensor) or steer_alpha.numel() != 1:
+            raise ValueError("steer_alpha: expected a one-element device tensor")
+        _arg(steer_alpha, torch.float32, tuple(steer_alpha.shape), "steer_alpha", device)
+    _arg(acc_out, torch.int32, (M, N), "acc_out", device)
     return Epilogue(_addr(bias), int(bool(gelu)), 0, _addr(residual), _addr(steer_dir), _addr(steer_alpha),
                     _addr(acc_out))
 
 
 def _ws(mode, M, K, N, ws, device):
     need = workspace_bytes(mode, M, K, N)
-    if ws is None and need:
-        ws = _torch().empty(need, dtype=_torch().uint8, device=device)
-    nbytes = 0 if ws is None else (ws.numel() * ws.element_size() if not isinstance(ws, int) else need)
-    return ws, nbytes
+    if ws is None:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=device) if need else None
+    elif not isinstance(ws, _torch().Tensor) or ws.device != device:
+        raise ValueError("ws: expected a tensor on the operands' device")
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
-def _out(x, N, y):
-    return _torch().empty((x.shape[0], N), dtype=_torch().float16, device=x.device) if y is None else y
+def _out(M, N, y, device, name="y"):
+    torch = _torch()
+    if y is None:
+        return torch.empty((M, N), dtype=torch.float16, device=device)
+    return _arg(y, torch.float16, (M, N), name, device)
 
 
 def qlinear_w8a8(x, wq, sw, y=None, ws=None, bias=None, gelu=False, residual=None, steer_dir=None,
                  steer_alpha=None, acc_out=None, stream=None):
     torch = _torch()
-    _dt(x, torch.float16, "x"), _dt(wq, torch.int8, "wq"), _dt(sw, torch.float16, "sw")
-    M, K = x.shape
-    N = wq.shape[0]
-    y = _out(x, N, y)
+    M, K = _mat(x, torch.float16, "x")
+    N, _ = _mat(wq, torch.int8, "wq")
+    _arg(wq, torch.int8, (N, K), "wq", x.device), _arg(sw, torch.float16, (N,), "sw", x.device)
+    y = _out(M, N, y, x.device)
+    e = _epi(M, N, x.device, bias, gelu, residual, steer_dir, steer_alpha, acc_out)
     ws, nb = _ws(ARIA_W8A8, M, K, N, ws, x.device)
-    e = _epi(bias, gelu, residual, steer_dir, steer_alpha, acc_out)
     _check(lib.aria_qlinear_w8a8(_addr(x), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e), _addr(y), _addr(ws),
                                  nb, _stream(stream)), "qlinear_w8a8")
     return y
 
 
+def _wxa16(bits, fn, name, x, wq, s, y, ws, bias, gelu, residual, steer_dir, steer_alpha, stream, group=None):
+    torch = _torch()
+    M, K = _mat(x, torch.float16, "x")
+    wtype = {8: torch.int8, 4: torch.uint8, 16: torch.float16}[bits]
+    N, _ = _mat(wq, wtype, "wq")
+    _arg(wq, wtype, (N, K // 2) if bits == 4 else (N, K), "wq", x.device)
+    if bits == 8:
+        _arg(s, torch.float16, (N,), "s", x.device)
+    elif bits == 4:
+        _arg(s, torch.float16, (N, K // 32), "s", x.device)
+    y = _out(M, N, y, x.device)
+    e = _epi(M, N, x.device, bias, gelu, residual, steer_dir, steer_alpha, None)
+    mode = {8: ARIA_W8A16, 4: ARIA_W4A16, 16: ARIA_W16A16}[bits]
+    ws, nb = _ws(mode, M, K, N, ws, x.device)
+    if bits == 16:
+        rc = fn(_addr(x), M, K, N, _addr(wq), ctypes.byref(e), _addr(y), _addr(ws), nb, _stream(stream))
+    elif bits == 4:
+        rc = fn(_addr(x), M, K, N, _addr(wq), _addr(s), group, ctypes.byref(e), _addr(y), _addr(ws), nb,
+                _stream(stream))
+    else:
+        rc = fn(_addr(x), M, K, N, _addr(wq), _addr(s), ctypes.byref(e), _addr(y), _addr(ws), nb, _stream(stream))
+    _check(rc, name)
+    return y
+
+
 def qlinear_w8a16(x, wq, sw, y=None, ws=None, bias=None, gelu=False, residual=None, steer_dir=None,
                   steer_alpha=None, stream=None):
-    torch = _torch()
-    _dt(x, torch.float16, "x"), _dt(wq, torch.int8, "wq"), _dt(sw, torch.float16, "sw")
-    M, K = x.shape
-    N = wq.shape[0]
-    y = _out(x, N, y)
-    ws, nb = _ws(ARIA_W8A16, M, K, N, ws, x.device)
-    e = _epi(bias, gelu, residual, steer_dir, steer_alpha, None)
-    _check(lib.aria_qlinear_w8a16(_addr(x), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e), _addr(y), _addr(ws),
-                                  nb, _stream(stream)), "qlinear_w8a16")
-    return y
+    return _wxa16(8, lib.aria_qlinear_w8a16, "qlinear_w8a16", x, wq, sw, y, ws, bias, gelu, residual, steer_dir,
+                  steer_alpha, stream)
 
 
 def qlinear_w4a16(x, wq4, sg, y=None, ws=None, bias=None, gelu=False, residual=None, steer_dir=None,
                   steer_alpha=None, stream=None, group: int = 32):
-    torch = _torch()
-    _dt(x, torch.float16, "x"), _dt(wq4, torch.uint8, "wq4"), _dt(sg, torch.float16, "sg")
-    M, K = x.shape
-    N = wq4.shape[0]
-    y = _out(x, N, y)
-    ws, nb = _ws(ARIA_W4A16, M, K, N, ws, x.device)
-    e = _epi(bias, gelu, residual, steer_dir, steer_alpha, None)
-    _check(lib.aria_qlinear_w4a16(_addr(x), M, K, N, _addr(wq4), _addr(sg), group, ctypes.byref(e), _addr(y),
-                                  _addr(ws), nb, _stream(stream)), "qlinear_w4a16")
-    return y
+    if group != 32:
+        raise ValueError(f"group must be 32, got {group}")
+    return _wxa16(4, lib.aria_qlinear_w4a16, "qlinear_w4a16", x, wq4, sg, y, ws, bias, gelu, residual, steer_dir,
+                  steer_alpha, stream, group)
 
 
 def qlinear_w16a16(x, wt, y=None, ws=None, bias=None, gelu=False, residual=None, steer_dir=None,
                    steer_alpha=None, stream=None):
     """The fp16 rung: Y = epilogue(X Wt^T) with Wt fp16 [N][K] from qpack(16, W)."""
-    torch = _torch()
-    _dt(x, torch.float16, "x"), _dt(wt, torch.float16, "wt")
-    M, K = x.shape
-    N = wt.shape[0]
-    y = _out(x, N, y)
-    ws, nb = _ws(ARIA_W16A16, M, K, N, ws, x.device)
-    e = _epi(bias, gelu, residual, steer_dir, steer_alpha, None)
-    _check(lib.aria_qlinear_w16a16(_addr(x), M, K, N, _addr(wt), ctypes.byref(e), _addr(y), _addr(ws), nb,
-                                   _stream(stream)), "qlinear_w16a16")
-    return y
+    return _wxa16(16, lib.aria_qlinear_w16a16, "qlinear_w16a16", x, wt, None, y, ws, bias, gelu, residual,
+                  steer_dir, steer_alpha, stream)
 
 
 def qlinear_grouped(bits: int, problems, stream=None):
@@ -247,15 +287,19 @@ def qlinear_grouped(bits: int, problems, stream=None):
     qlinear_w4a16).  bits 8 -> W8A16, bits 4 -> W4A16 (group 32).  Returns the
     list of outputs."""
     torch = _torch()
+    if bits not in (4, 8):
+        raise ValueError(f"bits must be 4 or 8, got {bits}")
     arr = (LinearProblem * len(problems))()
     keep, outs = [], []
+    wtype = torch.int8 if bits == 8 else torch.uint8
     for i, p in enumerate(problems):
         x, wq, s = p["x"], p["wq"], p["s"]
-        _dt(x, torch.float16, "x"), _dt(wq, torch.int8 if bits == 8 else torch.uint8, "wq"), _dt(s, torch.float16, "s")
-        M, K = x.shape
-        N = wq.shape[0]
-        y = _out(x, N, p.get("y"))
-        e = _epi(p.get("bias"), p.get("gelu", False), p.get("residual"), p.get("steer_dir"),
+        M, K = _mat(x, torch.float16, f"problems[{i}].x")
+        N, _ = _mat(wq, wtype, f"problems[{i}].wq")
+        _arg(wq, wtype, (N, K) if bits == 8 else (N, K // 2), f"problems[{i}].wq", x.device)
+        _arg(s, torch.float16, (N,) if bits == 8 else (N, K // 32), f"problems[{i}].s", x.device)
+        y = _out(M, N, p.get("y"), x.device, f"problems[{i}].y")
+        e = _epi(M, N, x.device, p.get("bias"), p.get("gelu", False), p.get("residual"), p.get("steer_dir"),
                  p.get("steer_alpha"), None)
         keep.append(e)
         outs.append(y)
@@ -268,9 +312,9 @@ def qlinear_grouped(bits: int, problems, stream=None):
 def layernorm(x, gamma, beta, eps: float = 1e-5, y=None, stream=None):
     """LayerNorm of every row of x fp16 [M][W] (y may be x)."""
     torch = _torch()
-    _dt(x, torch.float16, "x"), _dt(gamma, torch.float16, "gamma"), _dt(beta, torch.float16, "beta")
-    M, W = x.shape
-    y = torch.empty_like(x) if y is None else y
+    M, W = _mat(x, torch.float16, "x")
+    _arg(gamma, torch.float16, (W,), "gamma", x.device), _arg(beta, torch.float16, (W,), "beta", x.device)
+    y = torch.empty_like(x) if y is None else _arg(y, torch.float16, (M, W), "y", x.device)
     _check(lib.aria_layernorm(_addr(x), M, W, _addr(gamma), _addr(beta), float(eps), _addr(y), _stream(stream)),
            "layernorm")
     return y
@@ -282,12 +326,14 @@ def layernorm_quant(x, gamma, beta, eps: float = 1e-5, y=None, xq=None, sa=None,
     result in one pass: returns (xq, sa) or, with want_y / a given y,
     (y, xq, sa)."""
     torch = _torch()
-    _dt(x, torch.float16, "x"), _dt(gamma, torch.float16, "gamma"), _dt(beta, torch.float16, "beta")
-    M, W = x.shape
+    M, W = _mat(x, torch.float16, "x")
+    _arg(gamma, torch.float16, (W,), "gamma", x.device), _arg(beta, torch.float16, (W,), "beta", x.device)
     if y is None and want_y:
         y = torch.empty_like(x)
+    _arg(y, torch.float16, (M, W), "y", x.device)
     xq = torch.empty((M, W), dtype=torch.int8, device=x.device) if xq is None else xq
     sa = torch.empty((M,), dtype=torch.float16, device=x.device) if sa is None else sa
+    _arg(xq, torch.int8, (M, W), "xq", x.device), _arg(sa, torch.float16, (M,), "sa", x.device)
     _check(lib.aria_layernorm_quant(_addr(x), M, W, _addr(gamma), _addr(beta), float(eps), _addr(y), _addr(xq),
                                     _addr(sa), _stream(stream)), "layernorm_quant")
     return (xq, sa) if y is None else (y, xq, sa)
@@ -298,11 +344,12 @@ def qlinear_w8a8_prequant(xq, sa, wq, sw, y=None, bias=None, gelu=False, residua
     """The W8A8 linear on activations quantized beforehand (xq int8 [M][K],
     sa fp16 [M])."""
     torch = _torch()
-    _dt(xq, torch.int8, "xq"), _dt(sa, torch.float16, "sa"), _dt(wq, torch.int8, "wq"), _dt(sw, torch.float16, "sw")
-    M, K = xq.shape
-    N = wq.shape[0]
-    y = torch.empty((M, N), dtype=torch.float16, device=xq.device) if y is None else y
-    e = _epi(bias, gelu, residual, steer_dir, steer_alpha, acc_out)
+    M, K = _mat(xq, torch.int8, "xq")
+    _arg(sa, torch.float16, (M,), "sa", xq.device)
+    N, _ = _mat(wq, torch.int8, "wq")
+    _arg(wq, torch.int8, (N, K), "wq", xq.device), _arg(sw, torch.float16, (N,), "sw", xq.device)
+    y = _out(M, N, y, xq.device)
+    e = _epi(M, N, xq.device, bias, gelu, residual, steer_dir, steer_alpha, acc_out)
     _check(lib.aria_qlinear_w8a8_prequant(_addr(xq), _addr(sa), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e),
                                           _addr(y), _stream(stream)), "qlinear_w8a8_prequant")
     return y
@@ -312,9 +359,10 @@ def attention(qkv, heads: int, seq: int, out=None, stream=None):
     """Multi-head self-attention over [Q | K | V] = qkv fp16 [M][3W] within
     sequences of `seq` rows; returns out fp16 [M][W]."""
     torch = _torch()
-    _dt(qkv, torch.float16, "qkv")
-    M, W3 = qkv.shape
+    M, W3 = _mat(qkv, torch.float16, "qkv")
+    if W3 % 3:
+        raise ValueError(f"qkv: {W3} columns is not three blocks of equal width")
     W = W3 // 3
-    out = torch.empty((M, W), dtype=torch.float16, device=qkv.device) if out is None else out
+    out = _out(M, W, out, qkv.device, "out")
     _check(lib.aria_attention(_addr(qkv), M, W, int(heads), int(seq), _addr(out), _stream(stream)), "attention")
     return out
