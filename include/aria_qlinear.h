@@ -26,7 +26,8 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE memory owned by the caller unless stated otherwise.
- *     The library allocates nothing and keeps no state between calls.
+ *     The library allocates nothing and keeps no state between calls, except
+ *     the fixed device scratch of aria_qlinear_w8a8_noalloc.
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = null stream);
  *     they never synchronise and never read device memory on the host, so they
  *     may be captured into a HIP graph.
@@ -70,7 +71,9 @@ enum aria_status {
     ARIA_E_UNSUPPORTED = -4, /* bits not in {4, 8, 16}, group not 0 (8, 16) / 32 (4), or an option the call lacks */
     ARIA_E_WORKSPACE = -5,   /* workspace missing or smaller than required         */
     ARIA_E_HIP = -6,         /* the HIP runtime reported an error at launch        */
-    ARIA_E_ALIAS = -7        /* an output overlaps an input or another output      */
+    ARIA_E_ALIAS = -7,       /* an output overlaps an input or another output      */
+    ARIA_E_SCRATCH = -8      /* the shape needs more than the fixed scratch of the
+                                allocation-free call (ARIA_NOALLOC_SCRATCH_BYTES)   */
 };
 
 enum aria_mode { ARIA_W8A8 = 0, ARIA_W8A16 = 1, ARIA_W4A16 = 2, ARIA_W16A16 = 3 };
@@ -145,6 +148,30 @@ size_t aria_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, int64_t N);
 int aria_qlinear_w8a8(const void* x_f16, int64_t M, int64_t K, int64_t N,
                       const int8_t* wq, const void* s_w_f16, const aria_epilogue* epi,
                       void* y_f16, void* ws, size_t ws_bytes, aria_stream_t stream);
+
+/* Size of the library's fixed device scratch used by aria_qlinear_w8a8_noalloc
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define ARIA_NOALLOC_SCRATCH_BYTES (24u << 20)
+
+/* aria_qlinear_w8a8 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks and results as aria_qlinear_w8a8 (bit-identical Y
+ * and acc_out for the same inputs), but the quantized activations go to a
+ * file-scope device array of ARIA_NOALLOC_SCRATCH_BYTES bytes owned by the
+ * library instead of a caller workspace; the call allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine).  Limit: the shape's
+ * workspace, aria_qlinear_workspace_bytes(ARIA_W8A8, M, K, N) — Xq int8 [M][K]
+ * plus s_a fp16 [M], each rounded up to 256 bytes — must fit in the scratch,
+ * else ARIA_E_SCRATCH is returned and nothing is launched (M = 2048 allows
+ * K up to 12288).  The first call on a GPU looks up the array's device address
+ * there (ARIA_E_HIP if that fails).  Every call on one GPU uses the same array
+ * and leaves its contents behind (each call overwrites what it reads before
+ * reading it): calls that may overlap in time on one GPU — on different
+ * streams, or from different threads — race and must be serialised by the
+ * caller; aria_qlinear_w8a8 with a workspace per stream has no such limit. */
+int aria_qlinear_w8a8_noalloc(const void* x_f16, int64_t M, int64_t K, int64_t N,
+                              const int8_t* wq, const void* s_w_f16, const aria_epilogue* epi,
+                              void* y_f16, aria_stream_t stream);
 
 /* a3+a4+a5 — W8A16 (the pages' q8): Y = epilogue( s_w[n] * sum_k X[m][k] * Wq[n][k] )
  * with fp32 accumulation.  Reads the same Wq / s_w as W8A8. */

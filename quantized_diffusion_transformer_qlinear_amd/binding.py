@@ -45,6 +45,8 @@ lib.aria_qlinear_workspace_bytes.restype = _SZ
 for _name in ("aria_qlinear_w8a8", "aria_qlinear_w8a16"):
     getattr(lib, _name).argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P]
     getattr(lib, _name).restype = _I
+lib.aria_qlinear_w8a8_noalloc.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.POINTER(Epilogue), _P, _P]
+lib.aria_qlinear_w8a8_noalloc.restype = _I
 lib.aria_qlinear_w4a16.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P]
 lib.aria_qlinear_w4a16.restype = _I
 lib.aria_qlinear_w16a16.argtypes = [_P, _I64, _I64, _I64, _P, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P]
@@ -231,6 +233,21 @@ def qlinear_w8a8(x, wq, sw, y=None, ws=None, bias=None, gelu=False, residual=Non
     ws, nb = _ws(ARIA_W8A8, M, K, N, ws, x.device)
     _check(lib.aria_qlinear_w8a8(_addr(x), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e), _addr(y), _addr(ws),
                                  nb, _stream(stream)), "qlinear_w8a8")
+    return y
+
+
+def qlinear_w8a8_noalloc(x, wq, sw, y=None, bias=None, gelu=False, residual=None, steer_dir=None,
+                         steer_alpha=None, acc_out=None, stream=None):
+    """qlinear_w8a8 without a workspace: the library's fixed device scratch
+    holds the quantized activations (calls overlapping on one GPU race)."""
+    torch = _torch()
+    M, K = _mat(x, torch.float16, "x")
+    N, _ = _mat(wq, torch.int8, "wq")
+    _arg(wq, torch.int8, (N, K), "wq", x.device), _arg(sw, torch.float16, (N,), "sw", x.device)
+    y = _out(M, N, y, x.device)
+    e = _epi(M, N, x.device, bias, gelu, residual, steer_dir, steer_alpha, acc_out)
+    _check(lib.aria_qlinear_w8a8_noalloc(_addr(x), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e), _addr(y),
+                                         _stream(stream)), "qlinear_w8a8_noalloc")
     return y
 
 

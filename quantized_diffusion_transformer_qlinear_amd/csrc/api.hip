@@ -2,11 +2,22 @@
 // Host-side only: validates every argument before anything is launched, lays
 // out the caller's workspace, and enqueues the kernels on the caller's stream.
 // No allocation, no synchronisation, no device reads on the host.
+#include <atomic>
+#include <mutex>
+
 #include "../../include/aria_qlinear.h"
 #include "common.h"
 #include "kernels.h"
 
 using namespace aria;
+
+// The allocation-free W8A8 call keeps its quantized activations here: one copy
+// of this array per GPU, created when the library's code is loaded on that GPU
+// and held until the process ends.  In host code `scratch` names only a host
+// stand-in; its device address on the current GPU comes from
+// hipGetSymbolAddress (scratch_address below) and is the only form passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[ARIA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -74,6 +85,30 @@ bool epi_overlaps(const aria_epilogue* e, int64_t M, int64_t N, const void* p, s
            (e->steer_alpha && overlap(e->steer_alpha, 4, p, n)) || (e->acc_out && overlap(e->acc_out, mn * 4, p, n));
 }
 
+// Device address of `scratch` on the current GPU, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ARIA_E_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return ARIA_E_HIP;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return ARIA_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? ARIA_OK : ARIA_E_HIP; }
 
 }  // namespace
@@ -90,6 +125,7 @@ const char* aria_status_string(int s) {
         case ARIA_E_WORKSPACE: return "workspace missing or too small";
         case ARIA_E_HIP: return "HIP runtime error at launch";
         case ARIA_E_ALIAS: return "output overlaps an input";
+        case ARIA_E_SCRATCH: return "shape needs more than the library's fixed scratch (ARIA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -216,6 +252,17 @@ int aria_qlinear_w8a8(const void* x, int64_t M, int64_t K, int64_t N, const int8
         overlap(ws, need, wq, (size_t)(N * K)) || overlap(ws, need, sw, (size_t)N * 2) ||
         epi_overlaps(epi, M, N, ws, need))
         return ARIA_E_ALIAS;
+    return w8a8_launch(x, M, K, N, wq, sw, e, y, ws, static_cast<hipStream_t>(stream));
+}
+
+int aria_qlinear_w8a8_noalloc(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
+                              const aria_epilogue* epi, void* y, aria_stream_t stream) {
+    Epi e;
+    int rc = w8a8_check(x, M, K, N, wq, sw, epi, y, &e);
+    if (rc != ARIA_OK) return rc;
+    if (w8a8_ws(M, K) > (size_t)ARIA_NOALLOC_SCRATCH_BYTES) return ARIA_E_SCRATCH;
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws)) != ARIA_OK) return rc;
     return w8a8_launch(x, M, K, N, wq, sw, e, y, ws, static_cast<hipStream_t>(stream));
 }
 

@@ -29,7 +29,7 @@ def q():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (aria_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings(q):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert q.status_string(code) and q.status_string(code) != "unknown status"
     assert q.status_string(-99) == "unknown status"
     assert q.lib.aria_abi_version() == 1
@@ -109,6 +109,19 @@ def test_validation_codes(q):
     assert _w8a8(q, X, 64, 256, 256, W, S, E(9 << 20, 0, 0, None, None, None, (9 << 20) - 256), Y, WS, big) == -7
     assert L.aria_qlinear_w8a8_prequant(1 << 24, 2 << 24, 64, 256, 256, W, S,
                                         ctypes.byref(E(None, 0, 0, None, None, None, Y + 1024)), Y, None) == -7
+    # the allocation-free W8A8 call: the W8A8 checks, then the scratch limit,
+    # all before any device call
+    N0 = L.aria_qlinear_w8a8_noalloc
+    assert N0(None, 64, 256, 256, W, S, None, Y, None) == -1
+    assert N0(X, 64, 48, 256, W, S, None, Y, None) == -2
+    assert N0(X + 2, 64, 256, 256, W, S, None, Y, None) == -3
+    assert N0(X, 64, 256, 256, W, S, None, X + 1024, None) == -7
+    assert N0(X, 64, 256, 256, W, S, E(None, 2, 0, None, None, None, None), Y, None) == -4
+    assert N0(X, 64, 256, 256, W, S, E(None, 0, 0, None, None, None, Y + 256), Y, None) == -7
+    far = 1 << 36
+    assert N0(X, 2048, 12288, 256, W, S, None, far, None) == -8     # 24 MiB of int8 + the scales
+    assert N0(X, 4096, 8192, 256, W, S, None, far, None) == -8
+    assert N0(X, 1 << 20, 64, 64, W, S, None, far, None) == -8
     # acc_out only for W8A8; group must be 32 for W4A16
     ep = E(None, 0, 0, None, None, None, 6 << 20)
     assert L.aria_qlinear_w8a16(X, 64, 256, 256, W, S, ctypes.byref(ep), Y, None, 0, None) == -4

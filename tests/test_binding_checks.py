@@ -54,6 +54,8 @@ def test_w8a8_shapes(kw):
     args.update(kw)
     with pytest.raises(ValueError):
         q.qlinear_w8a8(**args)
+    with pytest.raises(ValueError):
+        q.qlinear_w8a8_noalloc(**args)
 
 
 @pytest.mark.parametrize("kw,err", [
