@@ -19,8 +19,8 @@ per-call breakdown and the dominant kernel's roofline every call is then
 captured alone (ten launches in one graph) and replayed between events on the
 replay stream: kernel time plus graph launch gaps, no host time.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--eager] [--no-extras] [--copy-calibration]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T] [--no-cpu-baseline]
+                       [--eager] [--serial] [--no-extras] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -129,6 +129,79 @@ def cpu_baseline(inputs, budget_s=12.0):
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"first {rows_done} of 2048 token rows of every linear of the step "
                       f"({ops / 1e9:.1f} G ops in {dt:.1f} s; plain C fp64/int64 oracle, OpenMP, {cpu})"}
+
+
+def cpu_stages(inputs, rows=64):
+    """Oracle wall time per stage on a row sample (seconds): packing of every
+    weight of the step (whole weights), per-token activation quantization,
+    the integer / fp64 contractions and the epilogues."""
+    import oracle
+    blk, lin2, x3, w3 = inputs
+    t = {"pack": 0.0, "act_quant": 0.0, "gemm": 0.0, "epilogue": 0.0}
+
+    def tick(stage, fn, *a, **k):
+        t0 = time.perf_counter()
+        r = fn(*a, **k)
+        t[stage] += time.perf_counter() - t0
+        return r
+    packed = {k: tick("pack", oracle.qpack8, blk[k]) for k in ("qkv", "o", "up", "down")}
+    p2 = tick("pack", oracle.qpack8, lin2.w)
+    p3 = tick("pack", oracle.qpack4, w3, 32)
+    # the step's linears, each on `rows` rows of its input
+    import synthetic_inputs as si
+    x_mlp = si.normal_f16((rows, blk["down"].shape[0]), 1.0, 599)   # a row sample of MLP-down's input width
+    for k in ("qkv", "o", "up", "down"):
+        x = x_mlp if k == "down" else blk["h"][:rows]
+        xq, sa = tick("act_quant", oracle.quant_act, x)
+        acc = tick("gemm", oracle.gemm_i8, xq, packed[k][0])
+        tick("epilogue", lambda: oracle.epilogue(oracle.scale_w8a8(acc, sa, packed[k][1]), gelu=(k == "up")))
+    r2 = tick("gemm", oracle.ref_w8a16, lin2.x[:rows], *p2)
+    tick("epilogue", oracle.epilogue, r2, bias=lin2.bias, gelu=True)
+    r3 = tick("gemm", oracle.ref_w4a16, x3[:rows], *p3)
+    tick("epilogue", oracle.epilogue, r3)
+    return {"rows": rows, "seconds": {k: round(v, 4) for k, v in t.items()},
+            "note": "pack: whole weights; the other stages on the first `rows` token rows of every linear"}
+
+
+def oracle_single_thread():
+    """Run in a child process with OMP_NUM_THREADS=1: the oracle on the
+    single-layer workloads (the 64x256x256 W8A8 linear in full; row samples of
+    the W8A16 MLP-up and of the W4A16 sweep) -> seconds and ops/s."""
+    import oracle
+    import synthetic_inputs as si
+    out = {}
+    c1 = si.small_w8a8()
+    pk = oracle.qpack8(c1.w)
+    t0 = time.perf_counter()
+    oracle.qlinear_w8a8(c1.x, *pk)
+    dt = time.perf_counter() - t0
+    out["w8a8_64x256x256"] = {"rows": 64, "s": round(dt, 4), "GOPS": round(2 * 64 * 256 * 256 / dt / 1e9, 3)}
+    lin2 = si.mlp_up_w8a16()
+    p2 = oracle.qpack8(lin2.w)
+    rows = 32
+    t0 = time.perf_counter()
+    oracle.qlinear_w8a16(lin2.x[:rows], *p2, bias=lin2.bias, gelu=True)
+    dt = time.perf_counter() - t0
+    out["w8a16_2048x1536x6144"] = {"rows": rows, "s": round(dt, 4), "GOPS": round(2 * rows * 1536 * 6144 / dt / 1e9, 3)}
+    x3, p3 = si.w4a16_sweep_x(), oracle.qpack4(si.w4a16_w(), 32)
+    for M in si.W4A16_M_SWEEP:
+        rows = min(M, 32)
+        t0 = time.perf_counter()
+        oracle.qlinear_w4a16(x3[:rows], *p3)
+        dt = time.perf_counter() - t0
+        out[f"w4a16_M{M}x1536x6144"] = {"rows": rows, "s": round(dt, 4),
+                                        "GOPS": round(2 * rows * 1536 * 6144 / dt / 1e9, 3)}
+    return out
+
+
+def cpu_single_thread():
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-single-thread-worker"], env=env,
+                       capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-400:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def graph_us(torch, fn, n=10, reps=5):
@@ -247,6 +320,50 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
     del cps, ys
     torch.cuda.synchronize()
     return res
+
+
+def w4a16_m256(q, torch, dev, x_rows, w, M=256, copies=120):
+    """The W4A16 1536 -> 6144 layer at M = 256 (near the fp16 ridge): `copies`
+    distinct packed weight / X / Y copies (1.1 GB, past the 256 MB last-level
+    cache) replayed as a graph of dependent launches; microseconds per layer,
+    TFLOP/s, algorithmic GB/s and the roofline fraction (MFMA-bound: the
+    arithmetic intensity, 523 flop/B, is past the fp16 ridge of 315)."""
+    K, N = w.shape
+    wd = torch.from_numpy(w).to(dev)
+    wq, sg = q.qpack(4, wd)
+    del wd
+    cps = [(wq.clone(), sg.clone(), torch.from_numpy(x_rows[:M].copy()).to(dev),
+            torch.empty((M, N), dtype=torch.float16, device=dev)) for _ in range(copies)]
+
+    def run_all():
+        for a, b, x, y in cps:
+            q.qlinear_w4a16(x, a, b, y=y)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        run_all()
+        with torch.cuda.graph(g, stream=st):
+            run_all()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / copies)
+    us = sorted(ts)[2]
+    flop = 2.0 * M * K * N
+    byt = algo_bytes("w4a16", M, K, N, 0)
+    tf = flop / us / 1e6
+    del cps, g
+    torch.cuda.synchronize()
+    return {"M": M, "K": K, "N": N, "copies": copies, "us_per_layer": round(us, 2), "tflops": round(tf, 1),
+            "GB/s": round(byt / us / 1e3, 1), "bytes": byt, "ai_flop_per_byte": round(flop / byt, 1),
+            "roofline": {"bound": "mfma", "peak": PEAK["fp16"], "unit": "TFLOP/s", "frac": round(tf / PEAK["fp16"], 4)}}
 
 
 def precision_ladder(q, torch, dev, lin2, x_small, reps=20):
@@ -438,7 +555,14 @@ def main():
                     help="skip the small-M streaming, precision-ladder, full-block and 1.2B-step measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed graph replays after the warm-up, for this long, before timing: the shader "
+                         "clock ramps up over the first ~50 steps after an idle period (reported as 'settle')")
+    ap.add_argument("--oracle-single-thread-worker", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.oracle_single_thread_worker:
+        print(json.dumps(oracle_single_thread()), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the qlinear path is data-parallel over tokens and "
               "runs unsharded on a single MI355X; run with --gpus 1.", file=sys.stderr)
@@ -530,6 +654,21 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
+    # untimed settle: replay (or run) the step until `settle_ms` of GPU time
+    # have passed, so the timed steps see the clock the step runs at
+    settle = {"replays": 0, "gpu_ms": 0.0}
+    if args.settle_ms > 0:
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        while settle["gpu_ms"] < args.settle_ms:
+            for _ in range(25):
+                graph.replay() if graph is not None else step()
+            settle["replays"] += 25
+            s1.record()
+            torch.cuda.synchronize()
+            settle["gpu_ms"] = s0.elapsed_time(s1)
+        settle["gpu_ms"] = round(settle["gpu_ms"], 1)
+
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -549,6 +688,22 @@ def main():
     call_fns["w8a16.up"] = lambda: q.qlinear_w8a16(x2, wq2, sw2, y=y2, bias=b2, gelu=True)
     call_fns["w4a16"] = lambda: q.qlinear_w4a16(x3d, wq3, sg3, y=y3)
     per = {n: graph_us(torch, call_fns[n]) for n in names}  # us per call
+
+    # W8A8 GEMM alone (quantized activations prepared beforehand): each layer's
+    # own input, quantized once, then the prequant call graph-replayed
+    W = si.WIDTH
+    xin = {"w8a8.qkv": q.quant_act(h), "w8a8.out": q.quant_act_columns(chain.qkv, 2 * W, W),
+           "w8a8.up": q.quant_act(chain.h1), "w8a8.down": q.quant_act(chain.u)}
+    ytmp = {n: torch.empty_like(buf) for n, buf in (("w8a8.qkv", chain.qkv), ("w8a8.out", chain.h1),
+                                                      ("w8a8.up", chain.u), ("w8a8.down", chain.out))}
+    gemm_fns = {
+        "w8a8.qkv": lambda: q.qlinear_w8a8_prequant(*xin["w8a8.qkv"], *packed["qkv"], y=ytmp["w8a8.qkv"]),
+        "w8a8.out": lambda: q.qlinear_w8a8_prequant(*xin["w8a8.out"], *packed["o"], y=ytmp["w8a8.out"], residual=h),
+        "w8a8.up": lambda: q.qlinear_w8a8_prequant(*xin["w8a8.up"], *packed["up"], y=ytmp["w8a8.up"], gelu=True),
+        "w8a8.down": lambda: q.qlinear_w8a8_prequant(*xin["w8a8.down"], *packed["down"], y=ytmp["w8a8.down"],
+                                                     residual=chain.h1, steer_dir=d, steer_alpha=alpha),
+    }
+    gemm_us = {n: graph_us(torch, fn) for n, fn in gemm_fns.items()}
 
     copy_us = None
     if args.copy_calibration:
@@ -593,6 +748,29 @@ def main():
     for k in ("achieved", "frac"):
         rf[k] = round(rf[k], 4 if k == "frac" else 1)
 
+    # the W8A8 layers against the int8 MFMA peak: GEMM alone and with the
+    # per-token quantization of their input (the headline target is stated for
+    # W8A8 at M = 2048)
+    w8 = [n for n in names if n.startswith("w8a8")]
+    w8_ops = {n: 2.0 * M * lin[n][1] * lin[n][2] for n in w8}
+    rw = {"bound": "mfma", "peak": PEAK["int8"], "unit": "TOPS", "per_layer": {}}
+    for n in w8:
+        mode, K, N, extra = lin[n]
+        t = read_traffic(n)
+        rw["per_layer"][n] = {
+            "gemm_us": round(gemm_us[n], 2), "gemm_tops": round(w8_ops[n] / gemm_us[n] / 1e6, 1),
+            "gemm_frac": round(w8_ops[n] / gemm_us[n] / 1e6 / PEAK["int8"], 4),
+            "with_act_quant_us": round(per[n], 2), "with_act_quant_frac": round(w8_ops[n] / per[n] / 1e6 / PEAK["int8"], 4),
+            "algorithmic_bytes": algo_bytes(mode, M, K, N, extra), "traffic": t,
+            "traffic_ratio": round(t / algo_bytes(mode, M, K, N, extra), 3) if t else None}
+    tot_ops = sum(w8_ops.values())
+    rw["achieved"] = round(tot_ops / sum(gemm_us[n] for n in w8) / 1e6, 1)
+    rw["frac"] = round(rw["achieved"] / PEAK["int8"], 4)
+    rw["with_act_quant"] = {"achieved": round(tot_ops / sum(per[n] for n in w8) / 1e6, 1)}
+    rw["with_act_quant"]["frac"] = round(rw["with_act_quant"]["achieved"] / PEAK["int8"], 4)
+    rw["note"] = ("achieved/frac: the four W8A8 GEMMs of the block alone (sum of ops / sum of graph-replayed "
+                  "times); with_act_quant: each call including its per-token quantization pass")
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -603,6 +781,9 @@ def main():
                                "(+bias, GELU) + W4A16 g32 1536x6144",
                    "tokens": M, "width": si.WIDTH, "mlp": si.MLP, "ops_per_step": total_ops},
         "roofline": rf,
+        "roofline_w8a8": rw,
+        "settle": dict(settle, why="untimed replays after the warm-up: the shader clock ramps up over the first "
+                                   "~50 steps after an idle period; steps and warmup keep their meaning"),
         "timing": ("eager launches" if graph is None else
                    "HIP graph replay of the step" + (" (W8A8 chain and weight-only layers as parallel branches)"
                                                      if concurrent else "")),
@@ -614,11 +795,14 @@ def main():
                                    "GB/s": round(2 * (256 << 20) / copy_us / 1e3, 1)}
     if not args.no_extras:
         out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
+        out["w4a16_m256"] = w4a16_m256(q, torch, dev, x3, w3)
         out["precision_ladder_1536x6144"] = precision_ladder(q, torch, dev, lin2, x3)
         out["dit_block_full_m2048"] = full_block(q, torch, dev, si, blk, packed)
         out["step_1p2b_m2048"] = step_1p2b(q, torch, dev, si)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
+        out["cpu_baseline"]["stages"] = cpu_stages((blk, lin2, x3, w3))
+        out["cpu_baseline"]["single_thread"] = cpu_single_thread()
     print(json.dumps(out), flush=True)
 
 
