@@ -28,12 +28,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 // zero tail past the row end is dropped; s_a by lane 0 at sa[m]).
 template <int CH>
 __device__ __forceinline__ void quantize_row(const v8h (&v)[CH], int lane, int m, rsrc_t rq, half_t* __restrict__ sa) {
-    float a = 0.0f;
+    // max |x|: the fp16 magnitude bits order like the magnitudes, so an
+    // integer max over (bits & 0x7FFF), two halves at a time, is exact
+    typedef unsigned short v2us __attribute__((ext_vector_type(2)));
+    v2us mx = {0, 0};
 #pragma unroll
-    for (int c = 0; c < CH; c++)
+    for (int c = 0; c < CH; c++) {
+        const v4u w = __builtin_bit_cast(v4u, v[c]);
 #pragma unroll
-        for (int e = 0; e < 8; e++) a = fmaxf(a, fabsf((float)v[c][e]));
-    a = wave_max(a);
+        for (int d = 0; d < 4; d++) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(v2us, w[d] & 0x7FFF7FFFu));
+    }
+    const float a = wave_max((float)__builtin_bit_cast(half_t, mx[0] > mx[1] ? mx[0] : mx[1]));
     const half_t sh = (half_t)(a / 127.0f);
     const float s = (float)sh;
     const float sdiv = s == 0.0f ? 1.0f : s;  // an all-zero row quantizes to zeros either way
@@ -41,29 +46,41 @@ __device__ __forceinline__ void quantize_row(const v8h (&v)[CH], int lane, int m
     if (lane == 0) sa[m] = sh;
 #pragma unroll
     for (int c = 0; c < CH; c++) {
+        // rint(x / s) without a division per element: f = x * RN(1/s) is
+        // within 127 * 2^-23 (~1.5e-5) of x / s, so rint(f) is rint(x / s)
+        // unless f lies within 2^-15 of a half-integer; for fp16 x and s that
+        // happens only at exact ties x = (k + 1/2) s, which are detected
+        // exactly (the FMA residual of the candidate k + 1/2 is exact and
+        // zero) and rounded from the exact half-integer, which rint sends to
+        // the even side.  The tie test runs only for chunks where some lane
+        // of the wave is near a half-integer.  Checked on the host against
+        // rint(x / s) in fp32 for every fp16 row maximum and every |x| <= it
+        // (1.0e9 pairs, 0 differ).
+        float f[8], q[8];
+        bool near = false;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            f[e] = (float)v[c][e] * rcp;
+            q[e] = __builtin_rintf(f[e]);
+            near |= fabsf(f[e] - q[e]) >= 0.5f - 0x1p-15f;
+        }
+        if (__builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float xv = (float)v[c][e];
+                const float qf = __builtin_floorf(f[e]) + 0.5f;
+                q[e] = __builtin_rintf(__builtin_fmaf(qf, sdiv, -xv) == 0.0f ? qf : f[e]);
+            }
+        }
         u32 w[2];
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            u32 packed = 0;
+            u32 b[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                // rint(x / s) without a division per element: x * RN(1/s)
-                // is within 2^-23 relative of x / s, and for fp16 x and s a
-                // quotient that is not exactly k + 1/2 lies at least ~3e-5
-                // from one, so rint(x * RN(1/s)) agrees except at exact ties;
-                // a tie x = (k + 1/2) s is detected exactly (the FMA residual
-                // of the candidate k + 1/2 is exact and zero) and rounded from
-                // the exact half-integer, which rint sends to the even side.
-                // Checked on the host against rint(x / s) in fp32 for every
-                // fp16 row maximum and every |x| <= it (1.0e9 pairs, 0 differ).
-                const float xv = (float)v[c][4 * h + e];
-                const float f = xv * rcp;
-                const float qf = __builtin_floorf(f) + 0.5f;
-                float r = __builtin_rintf(__builtin_fmaf(qf, sdiv, -xv) == 0.0f ? qf : f);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                packed |= ((u32)(int)r & 0xFFu) << (8 * e);
-            }
-            w[h] = packed;
+            for (int e = 0; e < 4; e++) b[e] = (u32)(int)fminf(fmaxf(q[4 * h + e], -127.0f), 127.0f);
+            // low bytes of the four codes, in order
+            w[h] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u),
+                                         __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u), 0x05040100u);
         }
         buf_store8_nt(v2u{w[0], w[1]}, rq, (uint32_t)(c * 512 + lane * 8));
     }

@@ -1,7 +1,8 @@
 """Host proof of the activation quantizer's division-free rounding (CPU only).
 
-The GPU kernel rounds x / s through a per-row reciprocal with an exact tie
-test instead of dividing per element.  quantizer_reciprocal_check.c replays
+The GPU kernel rounds x / s through a per-row reciprocal instead of dividing
+per element: rint(x * RN(1/s)), with an exact tie test only where the product
+lies within 2^-15 of a half-integer.  quantizer_reciprocal_check.c replays
 those fp32 steps for every fp16 row maximum and every |x| <= it and compares
 them with rint(x / s) under IEEE division; a mutant without the tie test must
 fail, which shows the check can see the cases that matter."""
@@ -39,4 +40,11 @@ def test_reciprocal_rounding_matches_division(tmp_path):
 
 def test_reciprocal_rounding_needs_the_tie_test(tmp_path):
     r = _run(_build(tmp_path, ("-DDROP_TIE_TEST",)))
+    assert r.returncode != 0 and "mismatches 0" not in r.stdout, r.stdout
+
+
+def test_fast_path_needs_its_margin(tmp_path):
+    """With a near-half-integer margin far below the product's error bound
+    (2^-30 instead of 2^-15), the fast path keeps wrong roundings."""
+    r = _run(_build(tmp_path, ("-DNEAR_MARGIN=0x1p-30f",)))
     assert r.returncode != 0 and "mismatches 0" not in r.stdout, r.stdout
