@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(HERE, "libaria_qlinear.so")
+# ARIA_QLINEAR_LIB selects another build of the same library (e.g. one whose
+# host code carries address and undefined-behaviour sanitizers)
+library_path = os.environ.get("ARIA_QLINEAR_LIB", os.path.join(HERE, "libaria_qlinear.so"))
 
 if not os.path.exists(library_path):
     raise ImportError(f"{library_path} is not built; run __graft_entry__.build() "

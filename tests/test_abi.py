@@ -10,7 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "aria_qlinear.h")
-LIB = os.path.join(ROOT, "quantized_diffusion_transformer_qlinear_amd", "libaria_qlinear.so")
+LIB = os.environ.get("ARIA_QLINEAR_LIB",
+                     os.path.join(ROOT, "quantized_diffusion_transformer_qlinear_amd", "libaria_qlinear.so"))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="HIP library not built")
 
