@@ -234,7 +234,7 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
     timed four ways: (1) one launch after the other copies ran (cold), (2) a
     graph of dependent single launches over the copies, (3) the same single
     launches as independent graph nodes, four parallel branches (copy j on
-    branch j % 4), (4) the grouped call over the copies (16 layers per
+    branch j % 4), (4) the grouped call over the copies (32 layers per
     launch) in a graph."""
     K, N = w.shape
     wd = torch.from_numpy(w).to(dev)

@@ -250,7 +250,7 @@ typedef struct aria_linear_problem {
 } aria_linear_problem;
 
 /* Several independent weight-only linears at small M in as few launches as
- * possible (one per 16 problems): the small-M regime of the 4-bit weights is
+ * possible (one per 32 problems): the small-M regime of the 4-bit weights is
  * bound by streaming them from memory (project page, "Results": 4-bit weights
  * for small devices), and one launch per layer leaves it bound by launch cost
  * instead.  bits 8 / group 0 runs W8A16, bits 4 / group 32 runs W4A16.

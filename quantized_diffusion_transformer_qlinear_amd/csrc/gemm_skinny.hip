@@ -17,6 +17,7 @@
 // loads: past K or M they read zero, so there are no branches) before it
 // decodes any of them; the four partial tiles are summed in LDS in a fixed
 // order, so results are deterministic.
+
 #include "common.h"
 #include "decode.h"
 #include "kernels.h"
@@ -26,6 +27,8 @@ namespace aria {
 // s_waitcnt immediate (gfx9 encoding): at most `vm` vector memory operations
 // and no LDS operations outstanding.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
+constexpr int kNS4 = 3;   // 4-bit weights: NS = 3 steps of 128 k per wave and chunk
 
 // K is cut into chunks of 4 * NS wave-steps (4 waves x NS steps x KPW k =
 // 1536 k at either width); in chunk c, wave w takes steps (4c + w) NS ..
@@ -236,6 +239,225 @@ __global__ __launch_bounds__(256) void gemm_skinny_grouped_kernel(SkinnyGroup g)
     skinny_finish<BITS, MT, CG>(part, acc, P.s, P.y, P.M, P.N, P.epi, n0, wave, lane);
 }
 
+// Streaming form of the grouped call for 4-bit weights at M <= 16 with K a
+// multiple of 256 up to one chunk (1536) and N a multiple of 8: persistent
+// workgroups, three per CU, each walk a contiguous run of units (32 output
+// channels of one problem over all of K), loading the next unit while they
+// decode one.
+//  - A unit's weights (32 rows x up to 768 bytes) are loaded in whole lines:
+//    each instruction moves 4 rows x 256 contiguous bytes (the register path
+//    of the kernels above moves 16 rows x 64 bytes per instruction, which
+//    streams ~25 % slower on MI355X).  The lanes then hold the wrong rows for
+//    the MFMA layout, so the unit passes through LDS: stored with an XOR
+//    swizzle, read back in the MFMA layout with 16 rows at one column landing
+//    in 16 different bank groups.  The group scales (32 rows x K/32,
+//    contiguous) travel the same way, and so do the epilogue operands.
+//  - Each wave takes the same K-quarter, steps and MFMA order as in the
+//    single-problem kernel and decodes the same bytes, and the four partial
+//    tiles are summed in LDS in the same order, so the results are
+//    bit-identical to one call per problem.
+//  - Each wave keeps its quarter of the activations in registers for the
+//    whole run (a workgroup's run never leaves its problem).
+//  - One unit in flight per workgroup and three workgroups per CU measured
+//    best: two units in flight per workgroup need two register sets, which
+//    leaves room for only two workgroups per CU, and streamed slower.
+constexpr int kStreamCh = 32;                 // output channels per unit
+constexpr int kStreamWB = kStreamCh * 768;    // weight bytes of a unit's LDS stage (K <= 1536)
+constexpr int kStreamSB = 4096;               // scale bytes of a stage (4 waves x 64 lanes x 16 bytes)
+constexpr int kStreamPerCU = 3;               // workgroups per CU (LDS 40 KB, 164 VGPRs each)
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// g.p[i].first is the first workgroup of problem i; each of its workgroups
+// takes `units_per_wg` consecutive units of that problem (the last one fewer
+// real units; the rest empty).  EPI: some problem of the group has a bias,
+// residual or steering operand (without, a unit loads only weights and
+// scales).
+template <bool EPI>
+__global__ __launch_bounds__(256, kStreamPerCU) void gemm_skinny_stream_kernel(SkinnyGroup g, int units_per_wg) {
+    constexpr int BITS = 4, MT = 1, CG = kStreamCh / 16, NS = kNS4;
+    using RG = SkinnyRegs<BITS, MT, CG, NS>;
+    // One weight and scale stage: it is refilled at the start of the next
+    // unit, after every wave has passed this unit's second barrier and so made
+    // its last weight read.  The epilogue pieces are read after that barrier,
+    // so they alternate between two small buffers.
+    constexpr int EPB = 1280;   // residual 1024 B, bias 64 B, direction 128 B, pad
+    __shared__ __attribute__((aligned(16))) char stage[kStreamWB + kStreamSB];
+    __shared__ __attribute__((aligned(16))) char epi[2][EPB];
+    __shared__ float part[4][MT * 16][16 * CG + 1];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = threadIdx.x % WAVE;
+    const int tid = (int)threadIdx.x;
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < kSkinnyGroupMax; i++)
+        if (i < g.count && (int)blockIdx.x >= g.p[i].first) pi = i;
+    const SkinnyProblem& P = g.p[pi];
+    const int nunits = (P.N + kStreamCh - 1) / kStreamCh;
+    // units [u0, uend) of problem pi; those past nunits are empty (their loads
+    // read zeros, nothing is stored), so the loop below has no conditional
+    // steps and the compiler's load counts stay exact
+    const int u0 = ((int)blockIdx.x - P.first) * units_per_wg;
+    const int uend = u0 + units_per_wg;
+    const uint32_t rowb = (uint32_t)P.K / 2, G = (uint32_t)P.K / 32;
+    const rsrc_t rw = make_rsrc(P.w, (uint32_t)P.N * rowb);
+    const rsrc_t rs = make_rsrc(P.s, (uint32_t)P.N * G * 2);
+    const rsrc_t ry = make_rsrc(P.y, (uint32_t)P.M * (uint32_t)P.N * 2);
+    const Epi& e = P.epi;
+    const bool steer = e.steer_dir && e.steer_alpha;
+    const rsrc_t rbias = make_rsrc(e.bias, e.bias ? (uint32_t)P.N * 2 : 0u);
+    const rsrc_t rres = make_rsrc(e.residual, e.residual ? (uint32_t)P.M * (uint32_t)P.N * 2 : 0u);
+    const rsrc_t rdir = make_rsrc(e.steer_dir, steer ? (uint32_t)P.N * 4 : 0u);
+    const rsrc_t ralpha = make_rsrc(e.steer_alpha, steer ? 4u : 0u);
+
+    // This lane's activations, loaded once: each wave reads only its quarter
+    // of K, the same runs as in the single-problem kernel (row lane % 16,
+    // k = kb + 8 q .. kb + 8 q + 7 for step j); zero past M and K.
+    v4i xr[NS][RG::NQ];
+    {
+        const rsrc_t rx = make_rsrc(P.x, (uint32_t)P.M * (uint32_t)P.K * 2);
+        const int m = lane % 16;
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            const int kb = (wave * NS + j) * RG::KPW + (lane / 16) * RG::KPL;
+#pragma unroll
+            for (int q = 0; q < RG::NQ; q++)
+                xr[j][q] = buf_load16(rx, m < P.M && kb + 8 * q < P.K ? ((uint32_t)m * P.K + kb + 8 * q) * 2 : OOB);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // A unit's loads, 16-byte pieces per lane: six of weights and one of
+    // scales, then (EPI) one each from the residual, the bias and the steering
+    // direction (the unit's 16 x 32 residual block is 64 pieces, held by
+    // threads 0..63; its 32 biases 4 pieces, threads 64..67; its 32 direction
+    // entries 8 pieces, threads 68..75; every other lane reads out of range).
+    // Every global read of a unit travels in this one stream of whole 16-byte
+    // register tuples: the load counter is in order, so a read issued late
+    // would wait for the unit in flight, and loop-carried values narrower than
+    // a tuple get split and copied at the loop's back edge, where each copy
+    // waits for its load.
+    constexpr int NL = EPI ? 10 : 7;
+    v4i RW[NL];
+    // Per-lane parts of the offsets, fixed for the whole run.  A unit adds
+    // only its first row; rows past N (the ragged last unit, the empty units)
+    // lie past the end of the weight, scale, bias and direction buffers and
+    // read zeros, and residual rows past M past the end of the residual, so
+    // no load depends on the unit being real (a predicate there turns into
+    // branches around the loads, and the compiler then waits for every load
+    // in flight at the join).  With N a multiple of 8 no 16-byte piece
+    // straddles column N; residual pieces of a ragged last unit's columns past
+    // N land in the next row, and their outputs are not stored.
+    uint32_t wofs[6];
+#pragma unroll
+    for (int i = 0; i < 6; i++) {
+        const int b = 6 * wave + i, rg = b / 3, seg = b % 3;      // block b: rows 4 rg .. 4 rg + 3, bytes 256 seg ..
+        const int r4 = lane / 16, c = (lane % 16) ^ (4 * (rg % 4) + r4);
+        const uint32_t byte = 256u * seg + 16u * c;
+        wofs[i] = byte < rowb ? (uint32_t)(4 * rg + r4) * rowb + byte : OOB;
+    }
+    const uint32_t sofs = (uint32_t)tid * 16;
+    const uint32_t sofs_ok = sofs < (uint32_t)kStreamCh * G * 2 ? sofs : OOB;
+    const uint32_t rofs = tid < 64 ? ((uint32_t)(tid / 4) * P.N + 8 * (tid % 4)) * 2 : OOB;
+    const uint32_t bofs = tid >= 64 && tid < 68 ? (uint32_t)(tid - 64) * 16 : OOB;
+    const uint32_t dofs = tid >= 68 && tid < 76 ? (uint32_t)(tid - 68) * 16 : OOB;
+    const float alpha = steer ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ralpha, 0, 0, 0)) : 0.0f;
+    // The prefetch past this workgroup's last unit (the loop's final pass) is
+    // pushed 2^21 rows out, past every buffer, so it costs no traffic; done
+    // with integer min / max, since a predicate here becomes a branch.
+    auto issue = [&](int u) {
+        const uint32_t n0 = (uint32_t)u * kStreamCh + (uint32_t)min(max(u - uend + 1, 0), 1) * (1u << 21);
+#pragma unroll
+        for (int i = 0; i < 6; i++) RW[i] = buf_load16(rw, wofs[i] + n0 * rowb);
+        RW[6] = buf_load16(rs, sofs_ok + n0 * G * 2);
+        if constexpr (EPI) {
+            RW[7] = buf_load16(rres, rofs + n0 * 2);
+            RW[8] = buf_load16(rbias, bofs + n0 * 2);
+            RW[9] = buf_load16(rdir, dofs + n0 * 4);
+        }
+    };
+
+    // Unit u's outputs from its four partial tiles (summed in the same order
+    // as skinny_finish) and the epilogue of epilogue_apply on the operands
+    // prefetched with the unit; thread o's outputs are rows o / 32 and
+    // o / 32 + 8 of column o % 32.  The stores are range-checked buffer
+    // stores, issued on every path (an out-of-range one is dropped).
+    auto finish = [&](int u) {
+        const bool real = u < nunits;
+        const char* ep = epi[(u - u0) & 1];
+        const int n0 = u * kStreamCh;
+        constexpr int OUTS = MT * 16 * kStreamCh / 256;
+#pragma unroll
+        for (int k = 0; k < OUTS; k++) {
+            const int o = tid + 256 * k;
+            const int row = o / kStreamCh, cc = o % kStreamCh, col = n0 + cc;
+            float v = ((part[0][row][cc] + part[1][row][cc]) + part[2][row][cc]) + part[3][row][cc];
+            if (EPI && e.bias) v += (float)*reinterpret_cast<const half_t*>(ep + 1024 + cc * 2);
+            if (e.gelu) v = gelu_tanh(v);
+            if (EPI && e.residual) v += (float)*reinterpret_cast<const half_t*>(ep + row * 64 + cc * 2);
+            if (EPI && alpha != 0.0f) v += alpha * *reinterpret_cast<const float*>(ep + 1088 + cc * 4);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (half_t)v), ry,
+                                                  (int)(real && row < P.M && col < P.N ? ((uint32_t)row * P.N + col) * 2 : OOB), 0, 0);
+        }
+    };
+
+    // Per unit: its loads into LDS, the next unit's loads issued, then the
+    // previous unit's outputs stored.  A store pending at a wait for loads
+    // makes the compiler wait for everything (loads and stores may complete
+    // out of order), so the stores go out right after the next loads and have
+    // a whole unit of decoding to complete in, instead of just before the
+    // wait as at the end of their own unit.
+    issue(u0);
+    for (int u = u0; u < uend; u++) {
+        // unit u into LDS: lane l of block b at slot l (the swizzle is in which
+        // bytes the lane loaded)
+#pragma unroll
+        for (int i = 0; i < 6; i++) *reinterpret_cast<v4i*>(stage + (6 * wave + i) * 1024 + lane * 16) = RW[i];
+        *reinterpret_cast<v4i*>(stage + kStreamWB + tid * 16) = RW[6];
+        // the epilogue pieces (threads 0..75): residual rows at 64-byte pitch,
+        // then bias, then direction
+        if constexpr (EPI)
+            if (tid < EPB / 16) *reinterpret_cast<v4i*>(epi[(u - u0) & 1] + tid * 16) = RW[7] | RW[8] | RW[9];
+        issue(u + 1);
+        if (u > u0) finish(u - 1);
+        lds_barrier();   // unit u in LDS; every wave is done with unit u - 1's partial tiles
+
+        v4f acc[CG];
+#pragma unroll
+        for (int c = 0; c < CG; c++) acc[c] = v4f{};
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+#pragma unroll
+            for (int c = 0; c < CG; c++) {
+                // this lane's run: row R of the unit, bytes B .. B + 15 of the row
+                const int R = 16 * c + lane % 16;
+                const int B = 192 * wave + 64 * j + 16 * (lane / 16);
+                const int rg = R / 4, r4 = R % 4, seg = B / 256, ch = (B % 256) / 16;
+                const int slot = 16 * r4 + (ch ^ (4 * (rg % 4) + r4));
+                const v4i w = *reinterpret_cast<const v4i*>(stage + (3 * rg + seg) * 1024 + slot * 16);
+                const int gi = (wave * NS + j) * 4 + lane / 16;
+                const u32 sb = *reinterpret_cast<const uint16_t*>(stage + kStreamWB + (R * (int)G + gi) * 2);
+                v4i d[RG::NQ];
+                dec4_bits(w, sb, d);
+#pragma unroll
+                for (int q = 0; q < RG::NQ; q++)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xr[j][q]),
+                                                                    __builtin_bit_cast(v8h, d[q]), acc[c], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CG; c++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) part[wave][4 * (lane / 16) + r][16 * c + lane % 16] = acc[c][r];
+        // unit u's partial tiles complete; every wave is done reading the stage
+        lds_barrier();
+    }
+    finish(uend - 1);
+}
+
 size_t wxa16_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
 
 namespace {
@@ -274,8 +496,41 @@ hipError_t launch_grouped_tiles(const SkinnyGroup& g, int tiles, hipStream_t st)
 
 }  // namespace
 
+// Every problem fits the streaming kernel: 4-bit, M <= 16, K % 256 == 0 and
+// K <= 1536 (one chunk, so a unit is all of K).
+bool stream_fits(int bits, const SkinnyGroup& g) {
+    if (bits != 4) return false;
+    for (int i = 0; i < g.count; i++)
+        if (g.p[i].M > 16 || g.p[i].K % 256 != 0 || g.p[i].K > 1536 || g.p[i].N % 8 != 0 || g.p[i].N > (1 << 20))
+            return false;
+    return true;
+}
+
 hipError_t launch_skinny_grouped(int bits, SkinnyGroup& g, hipStream_t st) {
     if (g.count < 1 || g.count > kSkinnyGroupMax) return hipErrorInvalidValue;
+    if (stream_fits(bits, g)) {
+        // persistent workgroups, each a run of one problem's units: about
+        // kStreamPerCU per CU in all
+        int units = 0;
+        bool epi = false;
+        for (int i = 0; i < g.count; i++) {
+            units += (g.p[i].N + kStreamCh - 1) / kStreamCh;
+            epi = epi || g.p[i].epi.bias || g.p[i].epi.residual || (g.p[i].epi.steer_dir && g.p[i].epi.steer_alpha);
+        }
+        int cus = 0, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        const int slots = kStreamPerCU * cus;
+        const int per = (units + slots - 1) / slots;
+        int wgs = 0;
+        for (int i = 0; i < g.count; i++) {
+            g.p[i].first = wgs;
+            wgs += ((g.p[i].N + kStreamCh - 1) / kStreamCh + per - 1) / per;
+        }
+        if (epi) hipLaunchKernelGGL(gemm_skinny_stream_kernel<true>, dim3(wgs), dim3(256), 0, st, g, per);
+        else hipLaunchKernelGGL(gemm_skinny_stream_kernel<false>, dim3(wgs), dim3(256), 0, st, g, per);
+        return hipGetLastError();
+    }
     int tiles = 0, maxm = 0;
     for (int i = 0; i < g.count; i++) {
         g.p[i].first = tiles;

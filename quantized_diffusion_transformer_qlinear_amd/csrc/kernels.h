@@ -39,7 +39,7 @@ size_t wxa16_workspace_bytes(int bits, int64_t M, int64_t K, int64_t N);
 // kSkinnyGroupMax problems, each problem's workgroups a slice of one grid.
 // The problem table travels as the kernel argument (no device memory); the
 // launcher fills in `first`.
-constexpr int kSkinnyGroupMax = 16;
+constexpr int kSkinnyGroupMax = 32;
 struct SkinnyProblem {
     const half_t* x;
     const uint8_t* w;

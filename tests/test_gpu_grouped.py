@@ -77,7 +77,7 @@ def test_grouped_mixed(q, bits):
 
 
 def test_grouped_more_than_one_launch(q):
-    """37 problems: three launches of at most 16; each equals its single call."""
+    """37 problems: two launches of at most 32; each equals its single call."""
     shapes = [(1 + (i * 7) % 64, 32 * (1 + i % 5), 1 + (i * 29) % 300) for i in range(37)]
     probs = [_problem(q, 4, M, K, N, 3000 + i) for i, (M, K, N) in enumerate(shapes)]
     log(f"grouped w4a16: {len(probs)} problems")
