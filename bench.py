@@ -311,7 +311,7 @@ def small_m_w4a16(q, torch, dev, x_rows, w, M=16, copies=200):
     res = {"M": M, "K": K, "N": N, "bytes_per_layer": layer_bytes, "copies": copies,
            "reading": "the 70% HBM target is read against 'graph_of_single_launches' (dependent launches); "
                       "'graph_of_independent_launches' runs the same launches as concurrent graph nodes; "
-                      "'grouped' is the one-launch-per-16-layers streaming path"}
+                      "'grouped' is the one-launch-per-32-layers streaming path"}
     for name, us in (("single_cold", med(cold)), ("graph_of_single_launches", out["graph_of_single_launches"]),
                      ("graph_of_independent_launches", out["graph_of_independent_launches"]),
                      ("grouped", out["grouped"])):
