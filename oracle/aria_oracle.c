@@ -12,12 +12,13 @@
  *        - "What aria is", bullet "Quantization that saves memory": weights are
  *          packed from fp16 down to 8 or 4 bits and the fp16 copy is released.
  *        - "Results", table "Quantization is close to free at 8-bit": the modes
- *          q8 (8-bit weights, fp16 activations), W8A8 (8-bit arithmetic on
- *          integer tensor cores) and q4 (4-bit weights).
+ *          q8 (8-bit weights, fp16 activations), W8A8 (8-bit operands
+ *          multiplied on the integer matrix units) and q4 (4-bit weights).
  *        - "Results", "Steering is real, inside a narrow window" and "Sonic
  *          seasoning": a direction is added to one transformer block's residual
  *          stream; strength 0 removes it with bit-identical output.
- *   [P2] chatpaper abstract: memory is saved "in place rather than adding to it".
+ *   [P2] chatpaper abstract: the quantized copy replaces the fp16 footprint
+ *        instead of adding to it.
  * The pages state the goal, not the formulas.  The formulas below are the plain
  * readings listed in the design notes (fp16 scales, absmax/qmax, round half to
  * even, qmax 127 / 7, group 32 along K, low nibble = even k, epilogue order
@@ -311,8 +312,8 @@ int or_scale_w8a8(const int32_t* acc, const uint16_t* sa, const uint16_t* sw,
 /* C-5  Epilogue, in place on y fp64 [M][N]:                                  */
 /*   y += bias[n];  y = gelu_tanh(y);  y += residual[m][n];  y += alpha*d[n]  */
 /* each step only when its operand is given; the steering term is skipped    */
-/* entirely when alpha == 0 or d is NULL ([P4] "Results": strength 0 gives   */
-/* bit-identical output).                                                    */
+/* entirely when alpha == 0 or d is NULL ([P4] "Results": zero strength     */
+/* leaves every output bit as without steering).                             */
 /* GELU, tanh form (Hendrycks & Gimpel, "Gaussian Error Linear Units"):      */
 /*   gelu(y) = 0.5 * y * (1 + tanh(sqrt(2/pi) * (y + 0.044715 * y^3)))       */
 /* ------------------------------------------------------------------------- */
