@@ -573,6 +573,8 @@ def main():
                     help="capture the step on one stream (no parallel branches)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the small-M streaming, precision-ladder, full-block and 1.2B-step measurements")
+    ap.add_argument("--extras", default="small_m,m256,ladder,block,step",
+                    help="comma-separated subset of the extra measurements to run (small_m, m256, ladder, block, step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--settle-ms", type=float, default=150.0,
@@ -580,6 +582,10 @@ def main():
                          "clock ramps up over the first ~50 steps after an idle period (reported as 'settle')")
     ap.add_argument("--oracle-single-thread-worker", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+    unknown = extras - {"small_m", "m256", "ladder", "block", "step"}
+    if unknown:
+        raise SystemExit(f"bench.py: unknown --extras {sorted(unknown)}")
     if args.oracle_single_thread_worker:
         print(json.dumps(oracle_single_thread()), flush=True)
         return
@@ -813,11 +819,15 @@ def main():
     if copy_us is not None:
         out["copy_calibration"] = {"bytes": 2 * (256 << 20), "us": round(copy_us, 2),
                                    "GB/s": round(2 * (256 << 20) / copy_us / 1e3, 1)}
-    if not args.no_extras:
+    if "small_m" in extras:
         out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
+    if "m256" in extras:
         out["w4a16_m256"] = w4a16_m256(q, torch, dev, x3, w3)
+    if "ladder" in extras:
         out["precision_ladder_1536x6144"] = precision_ladder(q, torch, dev, lin2, x3)
+    if "block" in extras:
         out["dit_block_full_m2048"] = full_block(q, torch, dev, si, blk, packed)
+    if "step" in extras:
         out["step_1p2b_m2048"] = step_1p2b(q, torch, dev, si)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline((blk, lin2, x3, w3))
