@@ -227,6 +227,38 @@ int aria_qlinear_w8a8_prequant(const int8_t* xq, const void* s_a_f16, int64_t M,
                                const int8_t* wq, const void* s_w_f16, const aria_epilogue* epi,
                                void* y_f16, aria_stream_t stream);
 
+/* a2 fused into the chain (per-token quantization of one W8A8 linear's
+ * input inside the linears around it; project page, "What aria is": the
+ * denoising step replayed as one graph, and "Results", the W8A8 row of the
+ * precision table).  The producer is aria_qlinear_w8a8
+ * that also records, for a later W8A8 linear reading columns
+ * [col0, col0 + ncols) of its output Y, the row maxima of those columns in
+ * 64-column blocks:
+ *   rowmax[m][j] = max over c in [col0 + 64 j, col0 + 64 j + 64) of
+ *                  (bits of the stored fp16 y[m][c]) & 0x7FFF
+ * (uint32 [M][ncols / 64]: the fp16 magnitude bits, which order like the
+ * magnitudes).  col0 and ncols are multiples of 64, ncols >= 64,
+ * col0 + ncols <= N, N % 8 == 0 (ARIA_E_SHAPE otherwise).  Y is bit-identical
+ * to aria_qlinear_w8a8 on the same arguments.  rowmax must not overlap any
+ * other argument (ARIA_E_ALIAS). */
+int aria_qlinear_w8a8_rowmax(const void* x_f16, int64_t M, int64_t K, int64_t N, const int8_t* wq,
+                             const void* s_w_f16, const aria_epilogue* epi, void* y_f16, void* ws,
+                             size_t ws_bytes, uint32_t* rowmax, int64_t col0, int64_t ncols,
+                             aria_stream_t stream);
+
+/* The consumer: the W8A8 linear over X fp16 [M][K] stored at row stride ldx
+ * halves (ldx >= K, ldx % 8 == 0; e.g. a column block of the producer's Y)
+ * whose per-token scales come from the producer's row maxima (rowmax uint32
+ * [M][K / 64], K % 64 == 0): s_a[m] = fp16(max_j rowmax[m][j] / 127), and X
+ * is quantized with the arithmetic of aria_quant_act while the contraction
+ * stages it, so no Xq is written.  Y, and s_a_out (fp16 [M], or NULL) when
+ * given, are bit-identical to aria_quant_act_strided on the same X followed
+ * by aria_qlinear_w8a8_prequant.  Needs no workspace; y must not overlap x or
+ * rowmax, and s_a_out must not overlap any other argument (ARIA_E_ALIAS). */
+int aria_qlinear_w8a8_fused(const void* x_f16, int64_t ldx, const uint32_t* rowmax, int64_t M, int64_t K,
+                            int64_t N, const int8_t* wq, const void* s_w_f16, const aria_epilogue* epi,
+                            void* y_f16, void* s_a_out_f16, aria_stream_t stream);
+
 /* Multi-head softmax self-attention: qkv fp16 [M][3W] holds [Q | K | V]
  * column blocks (the QKV linear's output), head h of each at columns
  * h*64 .. h*64+63; the M rows are M / seq independent sequences of seq rows.

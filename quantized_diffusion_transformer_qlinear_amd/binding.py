@@ -48,6 +48,11 @@ for _name in ("aria_qlinear_w8a8", "aria_qlinear_w8a16"):
     getattr(lib, _name).argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P]
     getattr(lib, _name).restype = _I
 lib.aria_qlinear_w8a8_noalloc.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.POINTER(Epilogue), _P, _P]
+lib.aria_qlinear_w8a8_rowmax.restype = _I
+lib.aria_qlinear_w8a8_rowmax.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P,
+                                         _I64, _I64, _P]
+lib.aria_qlinear_w8a8_fused.restype = _I
+lib.aria_qlinear_w8a8_fused.argtypes = [_P, _I64, _P, _I64, _I64, _I64, _P, _P, ctypes.POINTER(Epilogue), _P, _P, _P]
 lib.aria_qlinear_w8a8_noalloc.restype = _I
 lib.aria_qlinear_w4a16.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I, ctypes.POINTER(Epilogue), _P, _P, _SZ, _P]
 lib.aria_qlinear_w4a16.restype = _I
@@ -250,6 +255,51 @@ def qlinear_w8a8_noalloc(x, wq, sw, y=None, bias=None, gelu=False, residual=None
     e = _epi(M, N, x.device, bias, gelu, residual, steer_dir, steer_alpha, acc_out)
     _check(lib.aria_qlinear_w8a8_noalloc(_addr(x), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e), _addr(y),
                                          _stream(stream)), "qlinear_w8a8_noalloc")
+    return y
+
+
+def qlinear_w8a8_rowmax(x, wq, sw, col0: int, ncols: int, y=None, ws=None, rowmax=None, bias=None, gelu=False,
+                        residual=None, steer_dir=None, steer_alpha=None, acc_out=None, stream=None):
+    """qlinear_w8a8 that also records the row maxima of the output columns
+    [col0, col0 + ncols) in 64-column blocks (uint32 [M][ncols / 64], fp16
+    magnitude bits) for qlinear_w8a8_fused.  Returns (y, rowmax)."""
+    torch = _torch()
+    M, K = _mat(x, torch.float16, "x")
+    N, _ = _mat(wq, torch.int8, "wq")
+    _arg(wq, torch.int8, (N, K), "wq", x.device), _arg(sw, torch.float16, (N,), "sw", x.device)
+    if not (0 <= col0 and 64 <= ncols and col0 % 64 == 0 and ncols % 64 == 0 and col0 + ncols <= N):
+        raise ValueError(f"rowmax columns [{col0}, {col0 + ncols}) are not 64-column blocks inside [0, {N})")
+    y = _out(M, N, y, x.device)
+    rowmax = torch.empty((M, ncols // 64), dtype=torch.int32, device=x.device) if rowmax is None else rowmax
+    _arg(rowmax, torch.int32, (M, ncols // 64), "rowmax", x.device)
+    e = _epi(M, N, x.device, bias, gelu, residual, steer_dir, steer_alpha, acc_out)
+    ws, nb = _ws(ARIA_W8A8, M, K, N, ws, x.device)
+    _check(lib.aria_qlinear_w8a8_rowmax(_addr(x), M, K, N, _addr(wq), _addr(sw), ctypes.byref(e), _addr(y),
+                                        _addr(ws), nb, _addr(rowmax), int(col0), int(ncols), _stream(stream)),
+           "qlinear_w8a8_rowmax")
+    return y, rowmax
+
+
+def qlinear_w8a8_fused(src, col0: int, ncols: int, rowmax, wq, sw, y=None, sa_out=None, bias=None, gelu=False,
+                       residual=None, steer_dir=None, steer_alpha=None, acc_out=None, stream=None):
+    """The W8A8 linear over the column block src[:, col0:col0+ncols] of a
+    contiguous fp16 [M][W] tensor (read in place, row stride W), quantized
+    per token inside the contraction with the scales from `rowmax` (the
+    producer's qlinear_w8a8_rowmax output for exactly those columns)."""
+    torch = _torch()
+    M, W = _mat(src, torch.float16, "src")
+    if not (0 <= col0 and 0 < ncols and col0 + ncols <= W):
+        raise ValueError("column block outside the tensor")
+    K = ncols
+    N, _ = _mat(wq, torch.int8, "wq")
+    _arg(wq, torch.int8, (N, K), "wq", src.device), _arg(sw, torch.float16, (N,), "sw", src.device)
+    _arg(rowmax, torch.int32, (M, K // 64), "rowmax", src.device)
+    _arg(sa_out, torch.float16, (M,), "sa_out", src.device)
+    y = _out(M, N, y, src.device)
+    e = _epi(M, N, src.device, bias, gelu, residual, steer_dir, steer_alpha, acc_out)
+    _check(lib.aria_qlinear_w8a8_fused(_addr(src) + 2 * col0, W, _addr(rowmax), M, K, N, _addr(wq), _addr(sw),
+                                       ctypes.byref(e), _addr(y), _addr(sa_out), _stream(stream)),
+           "qlinear_w8a8_fused")
     return y
 
 

@@ -21,11 +21,17 @@ class DitBlockW8A8:
     """Preallocated W8A8 block: ``run(h)`` enqueues the chain on the stream and
     returns the block output (fp16 [M][width])."""
 
-    def __init__(self, packed: dict, M: int, width: int, mlp: int, steer_dir=None, steer_alpha=None):
+    def __init__(self, packed: dict, M: int, width: int, mlp: int, steer_dir=None, steer_alpha=None,
+                 fuse_out_quant: bool = False):
         import torch
         dev = packed["qkv"][0].device
         self.packed, self.M, self.width, self.mlp = packed, M, width, mlp
         self.steer_dir, self.steer_alpha = steer_dir, steer_alpha
+        # fuse_out_quant: the QKV linear records the V third's row maxima and
+        # the out-projection quantizes V inside its contraction (no separate
+        # quantization pass; bit-identical output)
+        self.fuse_out_quant = fuse_out_quant
+        self.rowmax = torch.empty((M, width // 64), dtype=torch.int32, device=dev) if fuse_out_quant else None
         f16 = torch.float16
         self.qkv = torch.empty((M, 3 * width), dtype=f16, device=dev)
         self.xq = torch.empty((M, width), dtype=torch.int8, device=dev)   # quantized V third
@@ -37,8 +43,20 @@ class DitBlockW8A8:
                    for k, n in ((width, 3 * width), (width, width), (width, mlp), (mlp, width)))
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
+    def _qkv(self, h, stream):
+        p = self.packed
+        if self.fuse_out_quant:
+            B.qlinear_w8a8_rowmax(h, *p["qkv"], 2 * self.width, self.width, y=self.qkv, ws=self.ws,
+                                  rowmax=self.rowmax, stream=stream)
+        else:
+            B.qlinear_w8a8(h, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)
+
     def _out(self, h, stream):
         # identity attention: the out-projection's input is the V third of qkv
+        if self.fuse_out_quant:
+            B.qlinear_w8a8_fused(self.qkv, 2 * self.width, self.width, self.rowmax, *self.packed["o"], y=self.h1,
+                                 residual=h, stream=stream)
+            return
         B.quant_act_columns(self.qkv, 2 * self.width, self.width, xq=self.xq, sa=self.sa, stream=stream)
         B.qlinear_w8a8_prequant(self.xq, self.sa, *self.packed["o"], y=self.h1, residual=h, stream=stream)
 
@@ -49,7 +67,7 @@ class DitBlockW8A8:
         activation quantization."""
         p = self.packed
         return [
-            ("qkv", lambda: B.qlinear_w8a8(h, *p["qkv"], y=self.qkv, ws=self.ws, stream=stream)),
+            ("qkv", lambda: self._qkv(h, stream)),
             ("out", lambda: self._out(h, stream)),
             ("up", lambda: B.qlinear_w8a8(self.h1, *p["up"], y=self.u, ws=self.ws, gelu=True, stream=stream)),
             ("down", lambda: B.qlinear_w8a8(self.u, *p["down"], y=self.out, ws=self.ws, residual=self.h1,

@@ -255,6 +255,57 @@ int aria_qlinear_w8a8(const void* x, int64_t M, int64_t K, int64_t N, const int8
     return w8a8_launch(x, M, K, N, wq, sw, e, y, ws, static_cast<hipStream_t>(stream));
 }
 
+int aria_qlinear_w8a8_rowmax(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
+                             const aria_epilogue* epi, void* y, void* ws, size_t ws_bytes, uint32_t* rowmax,
+                             int64_t col0, int64_t ncols, aria_stream_t stream) {
+    Epi e;
+    int rc = w8a8_check(x, M, K, N, wq, sw, epi, y, &e);
+    if (rc != ARIA_OK) return rc;
+    if (N % 8 != 0 || col0 < 0 || ncols < 64 || col0 % 64 != 0 || ncols % 64 != 0 || col0 + ncols > N)
+        return ARIA_E_SHAPE;
+    if (!rowmax) return ARIA_E_NULL;
+    if (!aligned16(ws) || !aligned16(rowmax)) return ARIA_E_ALIGN;
+    const size_t need = w8a8_ws(M, K);
+    if (!ws || ws_bytes < need) return ARIA_E_WORKSPACE;
+    const size_t rb = (size_t)M * (size_t)(ncols / 64) * 4;
+    if (overlap(ws, need, x, (size_t)(M * K) * 2) || overlap(ws, need, y, (size_t)(M * N) * 2) ||
+        overlap(ws, need, wq, (size_t)(N * K)) || overlap(ws, need, sw, (size_t)N * 2) ||
+        epi_overlaps(epi, M, N, ws, need) || overlap(rowmax, rb, ws, need) || overlap(rowmax, rb, x, (size_t)(M * K) * 2) ||
+        overlap(rowmax, rb, y, (size_t)(M * N) * 2) || overlap(rowmax, rb, wq, (size_t)(N * K)) ||
+        overlap(rowmax, rb, sw, (size_t)N * 2) || epi_overlaps(epi, M, N, rowmax, rb))
+        return ARIA_E_ALIAS;
+    e.rowmax = rowmax;
+    e.rowmax_ld = (int)(ncols / 64);
+    e.rowmax_c0 = (int)col0;
+    e.rowmax_c1 = (int)(col0 + ncols);
+    return w8a8_launch(x, M, K, N, wq, sw, e, y, ws, static_cast<hipStream_t>(stream));
+}
+
+int aria_qlinear_w8a8_fused(const void* x, int64_t ldx, const uint32_t* rowmax, int64_t M, int64_t K, int64_t N,
+                            const int8_t* wq, const void* sw, const aria_epilogue* epi, void* y, void* s_a_out,
+                            aria_stream_t stream) {
+    int rc = check_shape(M, K, N);
+    if (rc != ARIA_OK) return rc;
+    if (K % 64 != 0 || ldx < K || ldx % 8 != 0 || ldx > ((int64_t)1 << 40) / M || ldx >= ((int64_t)1 << 30))
+        return ARIA_E_SHAPE;
+    if (!x || !rowmax || !wq || !sw || !y) return ARIA_E_NULL;
+    if (!aligned16(x) || !aligned16(rowmax) || !aligned16(wq) || !aligned16(sw) || !aligned16(y) ||
+        !aligned16(s_a_out))
+        return ARIA_E_ALIGN;
+    const size_t xb = (size_t)((M - 1) * ldx + K) * 2, yb = (size_t)(M * N) * 2, rb = (size_t)(M * (K / 64)) * 4;
+    if (overlap(x, xb, y, yb) || overlap(rowmax, rb, y, yb) ||
+        (s_a_out && (overlap(s_a_out, (size_t)M * 2, y, yb) || overlap(s_a_out, (size_t)M * 2, x, xb) ||
+                     overlap(s_a_out, (size_t)M * 2, rowmax, rb) || overlap(s_a_out, (size_t)M * 2, wq, (size_t)(N * K)) ||
+                     overlap(s_a_out, (size_t)M * 2, sw, (size_t)N * 2) || epi_overlaps(epi, M, N, s_a_out, (size_t)M * 2))))
+        return ARIA_E_ALIAS;
+    Epi e;
+    if ((rc = make_epi(epi, ARIA_W8A8, M, N, y, &e)) != ARIA_OK) return rc;
+    const AQuant aq{rowmax, (int)(K / 64), (int)ldx, static_cast<half_t*>(s_a_out)};
+    (void)hipGetLastError();
+    return hip_status(launch_gemm_tiled(4, x, wq, static_cast<const half_t*>(sw), nullptr, static_cast<half_t*>(y),
+                                        (int)M, (int)N, (int)K, e, static_cast<hipStream_t>(stream), &aq));
+}
+
 int aria_qlinear_w8a8_noalloc(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq, const void* sw,
                               const aria_epilogue* epi, void* y, aria_stream_t stream) {
     Epi e;

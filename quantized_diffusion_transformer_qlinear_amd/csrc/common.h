@@ -27,6 +27,11 @@ struct Epi {
     const float* steer_alpha;  // device scalar or null
     int32_t* acc_out;        // W8A8 raw accumulators [M][N] or null
     int gelu;
+    // optional: row maxima of the stored output for a later per-token
+    // quantization of columns [rowmax_c0, rowmax_c1): rowmax[m * rowmax_ld + j]
+    // = the largest fp16 magnitude bits over columns rowmax_c0 + 64 j .. + 63
+    uint32_t* rowmax;
+    int rowmax_ld, rowmax_c0, rowmax_c1;
 };
 
 // GELU, tanh form (Hendrycks & Gimpel): 0.5 y (1 + tanh(u)), u = sqrt(2/pi)(y + 0.044715 y^3).

@@ -65,14 +65,22 @@ struct ModeT<3> {  // W16A16 (fp16 weights, the unquantized rung)
     static constexpr int KSTEP = 64, AEB = 2, KPB = 8, BCH = 8;
     typedef v16f acc_t;
 };
+template <>
+struct ModeT<4> {  // W8A8, X fp16 quantized per token as it is staged (A in LDS as int8)
+    static constexpr int KSTEP = 128, AEB = 2, KPB = 16, BCH = 8;
+    typedef v16i acc_t;
+};
 
 }  // namespace
 
 template <int MODE, int BM, int BN, int WM, int WN, int KS>
 __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const void* __restrict__ Aptr, const uint8_t* __restrict__ Bq,
                                                          const half_t* __restrict__ S, const half_t* __restrict__ sa,
-                                                         half_t* Y, int M, int N, int K, Epi epi) {
+                                                         half_t* Y, int M, int N, int K, Epi epi, AQuant aq) {
     using T = ModeT<MODE>;
+    constexpr bool I8 = MODE == 0 || MODE == 4;   // int8 operands on the integer matrix cores
+    constexpr bool QA = MODE == 4;                // A quantized per token while staged
+    constexpr int ACH = QA ? 16 : 8;              // 16-byte A chunks per row per K-step
     constexpr int NT = WM * WN * WAVE;
     constexpr int ROWB = 144;                    // LDS bytes per row (128 + pad)
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
                            (2 * BN * T::BCH) % (WM * WN * WAVE) == 0;
     constexpr int KPB = HALF4 ? T::KPB / 2 : T::KPB;   // k per packed B chunk
     constexpr int BCH = HALF4 ? 2 * T::BCH : T::BCH;   // packed B chunks per row per K-step
-    constexpr int NA = BM * 8;                   // 16-byte A chunks per K-step
+    constexpr int NA = BM * ACH;                 // 16-byte A chunks per K-step
     constexpr int NB = BN * BCH;                 // packed B chunks per K-step
     constexpr int LA = (NA + NT - 1) / NT;
     constexpr int LB = (NB + NT - 1) / NT;
@@ -113,7 +121,8 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     const int wm = wave / WN, wn = wave % WN;
     char(*const glds)[(BM + BN) * ROWB] = lds + 2 * grp;   // this group's two buffers
 
-    const uint32_t abytes = (uint32_t)M * (uint32_t)K * T::AEB;
+    const int lda = QA ? aq.lda : K;             // A row stride in elements
+    const uint32_t abytes = QA ? (uint32_t)((M - 1) * lda + K) * T::AEB : (uint32_t)M * (uint32_t)K * T::AEB;
     const uint32_t browb = MODE == 2 ? (uint32_t)K / 2 : MODE == 3 ? (uint32_t)K * 2 : (uint32_t)K;
     const rsrc_t ra = make_rsrc(Aptr, abytes);
     const rsrc_t rb = make_rsrc(Bq, (uint32_t)N * browb);
@@ -136,7 +145,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     // W4A16 12-wave tile and the 16-wave tile outside W8A8 lose 3-5 % with it,
     // so they keep the free schedule.  The 4-wave tiles (two register sets)
     // always pin.
-    constexpr bool PIN = NSET >= 2 || WM * WN == 8 || MODE == 0 || (WM * WN == 12 && MODE != 2);
+    constexpr bool PIN = NSET >= 2 || WM * WN == 8 || I8 || (WM * WN == 12 && MODE != 2);
     v4i RA[NSET][LA], RB[NSET][LB > 0 ? LB : 1];
     half_t RS[NSET][LB > 0 ? LB : 1];
 
@@ -146,9 +155,9 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     // count them exactly when it places its waits (a branch around a load
     // makes it wait for the loads of both paths); otherwise it is skipped.
     auto load_a = [&](int kt, int i, int set, bool ok) {
-        const int c = tid + i * NT, row = c / 8, ch = c % 8;
+        const int c = tid + i * NT, row = c / ACH, ch = c % ACH;
         const int k = (kt * KS + grp) * T::KSTEP + ch * (16 / T::AEB);
-        const uint32_t off = (uint32_t)(m0 + row) * (uint32_t)K * T::AEB + (uint32_t)k * T::AEB;
+        const uint32_t off = (uint32_t)(m0 + row) * (uint32_t)(QA ? lda : K) * T::AEB + (uint32_t)k * T::AEB;
         RA[set][i] = buf_load16(ra, ok && k < K && m0 + row < M ? off : OOB);
     };
     auto load_b = [&](int kt, int i, int set, bool ok) {
@@ -164,15 +173,50 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
         }
         if (MODE == 2) RS[set][i] = S[(int64_t)min(n0 + row, N - 1) * G + min(k, K - 32) / 32];
     };
+    // QA: this thread's A rows keep one scale each for the whole K loop
+    // (chunk i of the thread is in row (tid + i NT) / 16 at every K-step)
+    float qdiv[QA ? LA : 1], qrcp[QA ? LA : 1];
     auto store_a = [&](int buf, int i, int set) {
-        const int c = tid + i * NT, row = c / 8, ch = c % 8;
-        *reinterpret_cast<v4i*>(&glds[buf][row * ROWB + ch * 16]) = RA[set][i];
+        const int c = tid + i * NT, row = c / ACH, ch = c % ACH;
+        if constexpr (QA) {
+            // the per-token quantizer's arithmetic (rowops.h quantize_row) on
+            // these 8 values: rint(x * RN(1/s)), the exact tie test where a
+            // lane of the wave lands near a half-integer, clamp to +-127
+            const v8h x = __builtin_bit_cast(v8h, RA[set][i]);
+            float f[8], q[8];
+            bool near = false;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                f[e] = (float)x[e] * qrcp[i];
+                q[e] = __builtin_rintf(f[e]);
+                near |= fabsf(f[e] - q[e]) >= 0.5f - 0x1p-15f;
+            }
+            if (__builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float qf = __builtin_floorf(f[e]) + 0.5f;
+                    q[e] = __builtin_rintf(__builtin_fmaf(qf, qdiv[i], -(float)x[e]) == 0.0f ? qf : f[e]);
+                }
+            }
+            u32 w[2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                u32 b[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) b[e] = (u32)(int)fminf(fmaxf(q[4 * h + e], -127.0f), 127.0f);
+                w[h] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u),
+                                             __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u), 0x05040100u);
+            }
+            *reinterpret_cast<v2u*>(&glds[buf][row * ROWB + ch * 8]) = v2u{w[0], w[1]};
+        } else {
+            *reinterpret_cast<v4i*>(&glds[buf][row * ROWB + ch * 16]) = RA[set][i];
+        }
     };
     auto store_b = [&](int buf, int i, int set) {
         const int c = tid + i * NT;
         const int row = c / BCH, ch = c % BCH;
-        char* dst = &glds[buf][(BM + row) * ROWB + ch * (KPB * 2 / (MODE == 0 ? 2 : 1))];
-        if constexpr (MODE == 0 || MODE == 3) {
+        char* dst = &glds[buf][(BM + row) * ROWB + ch * (KPB * 2 / (I8 ? 2 : 1))];
+        if constexpr (I8 || MODE == 3) {
             *reinterpret_cast<v4i*>(dst) = RB[set][i];
         } else if constexpr (MODE == 1) {
             v4i lo, hi;
@@ -211,6 +255,35 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
         for (int i = p; i < LB; i += 4)
             if (has_b(i)) store_b(buf, i, set);
     };
+
+    // QA: the per-token scales of the tile's rows, from the producer's row
+    // maxima (four threads per row, an integer max over the fp16 magnitude
+    // bits as in the quantizer), then s_a = fp16(max / 127) and 1 / s_a as the
+    // quantizer computes them
+    __shared__ half_t qs[QA ? BM : 1];
+    if constexpr (QA) {
+        const int nslot = K / 64;
+        for (int r = (int)threadIdx.x; r < BM * 4; r += (int)blockDim.x) {
+            const int row = r / 4, part = r % 4, m = m0 + row;
+            uint32_t mx = 0;
+            if (m < M)
+                for (int j = part; j < nslot; j += 4) mx = max(mx, aq.amax[(int64_t)m * aq.amax_ld + j]);
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, WAVE));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, WAVE));
+            if (part == 0) {
+                const half_t sh = (half_t)((float)__builtin_bit_cast(half_t, (uint16_t)mx) / 127.0f);
+                qs[row] = sh;
+                if (aq.sa_out && tn == 0 && m < M) aq.sa_out[m] = sh;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < LA; i++) {
+            const float sf = (float)qs[min((tid + i * NT) / ACH, BM - 1)];
+            qdiv[i] = sf == 0.0f ? 1.0f : sf;   // an all-zero row quantizes to zeros either way
+            qrcp[i] = 1.0f / qdiv[i];
+        }
+    }
 
     typename T::acc_t acc[FM][FN];
 #pragma unroll
@@ -260,7 +333,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++) {
-                    if constexpr (MODE == 0)
+                    if constexpr (I8)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[p & 1][i], fb[p & 1][j], acc[i][j], 0, 0, 0);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fa[p & 1][i]),
@@ -325,7 +398,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const uint32_t v = park[((i * FN + j) * 16 + r) * WAVE];
-                    if constexpr (MODE == 0)
+                    if constexpr (I8)
                         acc[i][j][r] += (int32_t)v;
                     else
                         acc[i][j][r] += __builtin_bit_cast(float, v);
@@ -357,7 +430,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     const bool cvalid = COLFIX && vec_ok && colf + 8 <= N;
     float swf[8], bf[8], df[8];
     if constexpr (COLFIX) {
-        const v8h s8 = ((MODE == 0 || MODE == 1) && cvalid) ? *reinterpret_cast<const v8h*>(S + colf) : zero8;
+        const v8h s8 = ((I8 || MODE == 1) && cvalid) ? *reinterpret_cast<const v8h*>(S + colf) : zero8;
         const v8h b8 = (epi.bias && cvalid) ? *reinterpret_cast<const v8h*>(epi.bias + colf) : zero8;
         const v4f z4 = {};
         const v4f d0 = (alpha != 0.0f && cvalid) ? *reinterpret_cast<const v4f*>(epi.steer_dir + colf) : z4;
@@ -383,8 +456,8 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
             const int row = m0 + wm * WTM + i * 32 + rr, col = n0 + wn * WTN + cc * 8;
             const bool v = vec_ok && row < M && col + 8 <= N;
             const int64_t base = (int64_t)row * N + col;
-            sw8[t] = ((MODE == 0 || MODE == 1) && v && !COLFIX) ? *reinterpret_cast<const v8h*>(S + col) : zero8;
-            sr[t] = (MODE == 0 && v) ? (float)sa[row] : 0.0f;
+            sw8[t] = ((I8 || MODE == 1) && v && !COLFIX) ? *reinterpret_cast<const v8h*>(S + col) : zero8;
+            sr[t] = !(I8 && v) ? 0.0f : QA ? (float)qs[row - m0] : (float)sa[row];
             r8[t] = (epi.residual && v) ? *reinterpret_cast<const v8h*>(epi.residual + base) : zero8;
         }
         // 2) stage the raw accumulators of block-row i
@@ -408,7 +481,16 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
         for (int t = 0; t < TASKS; t++) {
             const int task = lane + t * WAVE, rr = task / CPRW, cc = task % CPRW;
             const int row = m0 + wm * WTM + i * 32 + rr, col = n0 + wn * WTN + cc * 8;
-            if (row >= M || col >= N) continue;
+            // row maxima for a later per-token quantization (W8A8 kernels with
+            // 64-column wave tiles only): the eight lanes of a row hold its 64
+            // columns, so the block's maximum is a reduction over those lanes
+            // (all lanes take part in the shuffles; lanes past M or N give 0)
+            constexpr bool RMX = MODE == 0 && CPRW == 8;
+            if constexpr (!RMX) {
+                if (row >= M || col >= N) continue;
+            }
+            uint32_t mbits = 0;
+            if (!RMX || (row < M && col < N)) {
             // read with the element type the staging stores used (a vector-typed
             // load of scalar-typed stores would let alias analysis drop them)
             uint32_t raw[8];
@@ -417,7 +499,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
             const int64_t base = (int64_t)row * N + col;
             if (vec_ok && col + 8 <= N) {
                 float v[8];
-                if constexpr (MODE == 0) {
+                if constexpr (I8) {
                     if (epi.acc_out) {
                         reinterpret_cast<v4u*>(epi.acc_out + base)[0] = v4u{raw[0], raw[1], raw[2], raw[3]};
                         reinterpret_cast<v4u*>(epi.acc_out + base)[1] = v4u{raw[4], raw[5], raw[6], raw[7]};
@@ -467,6 +549,15 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
                 v8h out;
 #pragma unroll
                 for (int e = 0; e < 8; e++) out[e] = (half_t)v[e];
+                if constexpr (RMX) {
+                    if (epi.rowmax) {
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            const half_t oe = out[e];   // copied out: see the staging note above
+                            mbits = max(mbits, (uint32_t)(__builtin_bit_cast(uint16_t, oe) & 0x7FFFu));
+                        }
+                    }
+                }
                 // non-temporal store: nothing in this launch reads the output
                 // again (measured on MI355X: +1-3 % per launch, +1.5 % on the
                 // DiT step, whose next kernel reads this output)
@@ -478,15 +569,26 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
                     if (col + e >= N) break;
                     const int64_t idx = base + e;
                     float v;
-                    if constexpr (MODE == 0) {
+                    if constexpr (I8) {
                         if (epi.acc_out) epi.acc_out[idx] = (int32_t)raw[e];
-                        v = (float)(int32_t)raw[e] * (float)sa[row] * (float)S[col + e];
+                        v = (float)(int32_t)raw[e] * (QA ? (float)qs[row - m0] : (float)sa[row]) * (float)S[col + e];
                     } else if constexpr (MODE == 1) {
                         v = __builtin_bit_cast(float, raw[e]) * (float)S[col + e];
                     } else {
                         v = __builtin_bit_cast(float, raw[e]);
                     }
                     Y[idx] = (half_t)epilogue_apply(v, idx, col + e, epi, alpha);
+                }
+            }
+            }
+            if constexpr (RMX) {
+                if (epi.rowmax) {
+                    mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 1, WAVE));
+                    mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 2, WAVE));
+                    mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 4, WAVE));
+                    const int c64 = n0 + wn * WTN;   // this wave's 64 columns
+                    if (cc == 0 && row < M && c64 >= epi.rowmax_c0 && c64 < epi.rowmax_c1)
+                        epi.rowmax[(int64_t)row * epi.rowmax_ld + (c64 - epi.rowmax_c0) / 64] = mbits;
                 }
             }
         }
@@ -542,44 +644,57 @@ int num_cus() {
     return cus;
 }
 
-const TileCfg& pick_tile(int mode, int M, int N, int K) {
+// The fused-quantization form (mode 4) holds twice the A chunks in
+// registers: on the 12- and 16-wave tiles and the K-split 128x128 tile it
+// spills, so it does not use them.
+bool tile_ok(const TileCfg& t, int mode, bool wave64) {
+    if (wave64 && t.bn / t.wn != 64) return false;
+    if (mode == 4 && (t.wm * t.wn >= 12 || t.ks > 1)) return false;
+    return true;
+}
+
+// wave64: only tiles whose waves are 64 columns wide (the row-maxima output)
+const TileCfg& pick_tile(int mode, int M, int N, int K, bool wave64 = false) {
     const char* env = getenv("ARIA_QLINEAR_TILE");  // "BMxBNxWMxWN[xKS]" tuning override
     if (env) {
         int bm = 0, bn = 0, wm = 0, wn = 0, ks = 1;
         if (sscanf(env, "%dx%dx%dx%dx%d", &bm, &bn, &wm, &wn, &ks) >= 4)
             for (const TileCfg& t : kTiles)
-                if (t.bm == bm && t.bn == bn && t.wm == wm && t.wn == wn && t.ks == ks) return t;
+                if (t.bm == bm && t.bn == bn && t.wm == wm && t.wn == wn && t.ks == ks && tile_ok(t, mode, wave64))
+                    return t;
     }
+    const int em = mode == 4 ? 0 : mode;   // the fused-quantization form is priced as W8A8
     const int cus = num_cus();
     double best = 1e300;
-    const TileCfg* pick = &kTiles[0];
+    const TileCfg* pick = nullptr;
     for (const TileCfg& t : kTiles) {
+        if (!tile_ok(t, mode, wave64)) continue;
         const long tiles = (long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
         // the K split pays only where the 4-wave tile would leave one
         // workgroup (one wave per SIMD) on each CU, and over a long enough K
         if (t.ks > 1 && (tiles > cus || K < 1024)) continue;
         const long waves = (tiles + cus - 1) / cus;
-        const double cost = (double)waves * t.bm * t.bn / t.eff[mode];
+        const double cost = (double)waves * t.bm * t.bn / t.eff[em];
         if (cost < best) best = cost, pick = &t;
     }
-    return *pick;
+    return *pick;   // every filter leaves at least the 4-wave 64-column 128x128 tile
 }
 
 template <int MODE, int BM, int BN, int WM, int WN, int KS>
 hipError_t launch_one(const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y, int M, int N,
-                      int K, const Epi& e, hipStream_t st) {
+                      int K, const Epi& e, hipStream_t st, const AQuant& aq) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL((gemm_tiled_kernel<MODE, BM, BN, WM, WN, KS>), dim3(tiles), dim3(WM * WN * KS * WAVE), 0, st, a,
-                       b, s, sa, y, M, N, K, e);
+                       b, s, sa, y, M, N, K, e, aq);
     return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const half_t* s, const half_t* sa, half_t* y,
-                       int M, int N, int K, const Epi& e, hipStream_t st) {
+                       int M, int N, int K, const Epi& e, hipStream_t st, const AQuant& aq) {
 #define ARIA_TILE(BM_, BN_, WM_, WN_, KS_)                                     \
     if (t.bm == BM_ && t.bn == BN_ && t.wm == WM_ && t.wn == WN_ && t.ks == KS_) \
-        return launch_one<MODE, BM_, BN_, WM_, WN_, KS_>(a, b, s, sa, y, M, N, K, e, st);
+        return launch_one<MODE, BM_, BN_, WM_, WN_, KS_>(a, b, s, sa, y, M, N, K, e, st, aq);
     ARIA_TILE(256, 192, 4, 3, 1) ARIA_TILE(256, 256, 4, 4, 1) ARIA_TILE(256, 192, 4, 2, 1) ARIA_TILE(256, 128, 4, 2, 1)
     ARIA_TILE(128, 256, 2, 4, 1) ARIA_TILE(128, 192, 2, 2, 1) ARIA_TILE(128, 128, 2, 2, 1) ARIA_TILE(64, 192, 2, 2, 1)
     ARIA_TILE(128, 64, 2, 2, 1) ARIA_TILE(64, 128, 2, 2, 1) ARIA_TILE(64, 64, 2, 2, 1)
@@ -591,25 +706,32 @@ hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const 
 }  // namespace
 
 hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half_t* s, const half_t* sa, half_t* y,
-                             int M, int N, int K, const Epi& epi, hipStream_t st) {
+                             int M, int N, int K, const Epi& epi, hipStream_t st, const AQuant* aq) {
+    if (mode == 4 && !aq) return hipErrorInvalidValue;
     // 32-bit buffer offsets: split very tall problems into row blocks
     const int64_t aeb = mode == 0 ? 1 : 2;
-    const int64_t max_rows = ((int64_t)1 << 31) / ((int64_t)K * aeb) / 256 * 256;
-    const TileCfg& t = pick_tile(mode, M > max_rows ? (int)max_rows : M, N, K);
+    const int64_t lda = mode == 4 ? aq->lda : K;
+    const int64_t max_rows = ((int64_t)1 << 31) / ((int64_t)lda * aeb) / 256 * 256;
+    const TileCfg& t = pick_tile(mode, M > max_rows ? (int)max_rows : M, N, K, epi.rowmax != nullptr);
     const uint8_t* b = static_cast<const uint8_t*>(bq);
     for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
         const int rows = (int)((M - r0) < max_rows ? (M - r0) : max_rows);
         Epi e = epi;
         if (e.residual) e.residual += r0 * N;
         if (e.acc_out) e.acc_out += r0 * N;
-        const char* ar = static_cast<const char*>(a) + r0 * K * aeb;
+        if (e.rowmax) e.rowmax += r0 * e.rowmax_ld;
+        AQuant q = aq ? *aq : AQuant{nullptr, 0, 0, nullptr};
+        if (q.amax) q.amax += r0 * q.amax_ld;
+        if (q.sa_out) q.sa_out += r0;
+        const char* ar = static_cast<const char*>(a) + r0 * lda * aeb;
         const half_t* sar = sa ? sa + r0 : nullptr;
         half_t* yr = y + r0 * N;
         hipError_t err;
-        if (mode == 0) err = launch_mode<0>(t, ar, b, s, sar, yr, rows, N, K, e, st);
-        else if (mode == 1) err = launch_mode<1>(t, ar, b, s, sar, yr, rows, N, K, e, st);
-        else if (mode == 2) err = launch_mode<2>(t, ar, b, s, sar, yr, rows, N, K, e, st);
-        else err = launch_mode<3>(t, ar, b, s, sar, yr, rows, N, K, e, st);
+        if (mode == 0) err = launch_mode<0>(t, ar, b, s, sar, yr, rows, N, K, e, st, q);
+        else if (mode == 1) err = launch_mode<1>(t, ar, b, s, sar, yr, rows, N, K, e, st, q);
+        else if (mode == 2) err = launch_mode<2>(t, ar, b, s, sar, yr, rows, N, K, e, st, q);
+        else if (mode == 3) err = launch_mode<3>(t, ar, b, s, sar, yr, rows, N, K, e, st, q);
+        else err = launch_mode<4>(t, ar, b, s, sar, yr, rows, N, K, e, st, q);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

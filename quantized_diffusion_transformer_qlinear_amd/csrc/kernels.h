@@ -21,10 +21,22 @@ hipError_t launch_layernorm_quant(const half_t* x, const half_t* gamma, const ha
 hipError_t launch_attention(const half_t* qkv, int64_t M, int64_t W, int64_t H, int64_t S, half_t* out,
                             hipStream_t st);
 
+// Per-token quantization inside the W8A8 contraction (mode 4): A is X fp16
+// with row stride lda (halves); row m's scale comes from the row maxima a
+// producing epilogue recorded (amax[m * amax_ld + j], j < K / 64, fp16
+// magnitude bits); sa_out (or null) receives the scales.
+struct AQuant {
+    const uint32_t* amax;
+    int amax_ld, lda;
+    half_t* sa_out;
+};
+
 // Tiled contraction + epilogue for all modes (gemm_tiled.hip).  mode 0 = W8A8
-// (a = Xq int8 [M][K], sa = per-token scales), 1 = W8A16, 2 = W4A16 (a = X fp16).
+// (a = Xq int8 [M][K], sa = per-token scales), 1 = W8A16, 2 = W4A16 (a = X fp16),
+// 3 = W16A16, 4 = W8A8 quantizing a = X fp16 on the way in (aq required).
+// With epi.rowmax set, only tiles whose waves are 64 columns wide are used.
 hipError_t launch_gemm_tiled(int mode, const void* a, const void* bq, const half_t* s, const half_t* sa, half_t* y,
-                             int M, int N, int K, const Epi& epi, hipStream_t st);
+                             int M, int N, int K, const Epi& epi, hipStream_t st, const AQuant* aq = nullptr);
 
 // Weight-only contraction + epilogue: A = X fp16 [M][K]; bits 8: B = Wq int8 [N][K] with
 // per-channel scales s [N]; bits 4: B = Wq4 [N][K/2] with group scales s [N][K/32];

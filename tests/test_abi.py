@@ -30,7 +30,7 @@ def q():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (aria_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -180,6 +180,45 @@ def test_validation_codes(q):
     assert L.aria_attention(X, 64, 128, 2, 32, Y + 8, None) == -3
     assert L.aria_qlinear_workspace_bytes(9, 64, 64, 64) == 0
     assert L.aria_qlinear_workspace_bytes(0, 64, 40, 64) == 0
+
+
+def test_fused_quant_validation_codes(q):
+    """The producer (W8A8 + row maxima of a column block) and the consumer
+    (W8A8 quantizing its fp16 input with those maxima): every rejection on the
+    host, before any launch."""
+    L = q.lib
+    X, W, S, Y, WS, R = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 6 << 20
+    big = 1 << 40
+    P = L.aria_qlinear_w8a8_rowmax
+    # the W8A8 checks first
+    assert P(None, 64, 256, 768, W, S, None, Y, WS, big, R, 512, 256, None) == -1
+    assert P(X, 64, 48, 768, W, S, None, Y, WS, big, R, 512, 256, None) == -2
+    # the column block: 64-column blocks inside [0, N), N % 8 == 0
+    for c0, nc in ((512, 0), (512, 32), (500, 256), (512, 200), (640, 256), (-64, 128)):
+        assert P(X, 64, 256, 768, W, S, None, Y, WS, big, R, c0, nc, None) == -2, (c0, nc)
+    assert P(X, 64, 256, 772, W, S, None, Y, WS, big, R, 512, 256, None) == -2         # N % 8
+    assert P(X, 64, 256, 768, W, S, None, Y, WS, big, None, 512, 256, None) == -1
+    assert P(X, 64, 256, 768, W, S, None, Y, WS, big, R + 4, 512, 256, None) == -3
+    assert P(X, 64, 256, 768, W, S, None, Y, WS, 100, R, 512, 256, None) == -5
+    # rowmax may overlap nothing else
+    for r in (X + 64, Y + 1024, WS + 256, W + 64, S - 128):
+        assert P(X, 64, 256, 768, W, S, None, Y, WS, big, r, 512, 256, None) == -7, hex(r)
+    E = q.binding.Epilogue
+    assert P(X, 64, 256, 768, W, S, E(None, 0, 0, R + 64, None, None, None), Y, WS, big, R, 512, 256, None) == -7
+    F = L.aria_qlinear_w8a8_fused
+    # (x, ldx, rowmax, M, K, N, wq, sw, epi, y, s_a_out, stream)
+    assert F(None, 768, R, 64, 256, 256, W, S, None, Y, None, None) == -1
+    assert F(X, 768, None, 64, 256, 256, W, S, None, Y, None, None) == -1
+    assert F(X, 768, R, 64, 224, 256, W, S, None, Y, None, None) == -2       # K % 64
+    assert F(X, 192, R, 64, 256, 256, W, S, None, Y, None, None) == -2       # ldx < K
+    assert F(X, 772, R, 64, 256, 256, W, S, None, Y, None, None) == -2       # ldx % 8
+    assert F(X + 2, 768, R, 64, 256, 256, W, S, None, Y, None, None) == -3
+    assert F(X, 768, R, 64, 256, 256, W, S, None, Y, 7 << 20 | 2, None) == -3
+    assert F(X, 768, R, 64, 256, 256, W, S, None, X + 4096, None, None) == -7        # y inside the rows read
+    assert F(X, 768, R, 64, 256, 256, W, S, None, R + 64, None, None) == -7          # y over rowmax
+    for sa in (Y + 64, X + 1024, R + 16, W + 64, S - 64):
+        assert F(X, 768, R, 64, 256, 256, W, S, None, Y, sa, None) == -7, hex(sa)
+    assert F(X, 768, R, 64, 256, 256, W, S, E(None, 2, 0, None, None, None, None), Y, None, None) == -4
 
 
 def test_grouped_validation_codes(q):
