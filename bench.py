@@ -573,8 +573,9 @@ def main():
                     help="capture the step on one stream (no parallel branches)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the small-M streaming, precision-ladder, full-block and 1.2B-step measurements")
-    ap.add_argument("--extras", default="small_m,m256,ladder,block,step",
-                    help="comma-separated subset of the extra measurements to run (small_m, m256, ladder, block, step)")
+    ap.add_argument("--extras", default="fusion,small_m,m256,ladder,block,step",
+                    help="comma-separated subset of the extra measurements to run "
+                         "(fusion, small_m, m256, ladder, block, step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--settle-ms", type=float, default=150.0,
@@ -583,7 +584,7 @@ def main():
     ap.add_argument("--oracle-single-thread-worker", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
-    unknown = extras - {"small_m", "m256", "ladder", "block", "step"}
+    unknown = extras - {"fusion", "small_m", "m256", "ladder", "block", "step"}
     if unknown:
         raise SystemExit(f"bench.py: unknown --extras {sorted(unknown)}")
     if args.oracle_single_thread_worker:
@@ -731,6 +732,34 @@ def main():
     }
     gemm_us = {n: graph_us(torch, fn) for n, fn in gemm_fns.items()}
 
+    # The per-token quantization fused into the linears around it, on the
+    # chain's out-projection (the V third of QKV): QKV recording the row
+    # maxima of that third, and the out-projection quantizing it in its
+    # contraction, against the separate strided quantization pass + the
+    # linear on int8 input.  Same output bits either way (tested).
+    fusion = None
+    if "fusion" in extras:
+        W = si.WIDTH
+        fchain = DitBlockW8A8(packed, M, W, si.MLP, steer_dir=d, steer_alpha=alpha, fuse_out_quant=True)
+        fchain.run(h)
+        parts = {
+            "qkv (plain)": lambda: q.qlinear_w8a8(h, *packed["qkv"], y=chain.qkv, ws=chain.ws),
+            "qkv (+ row maxima of the V third)": lambda: q.qlinear_w8a8_rowmax(
+                h, *packed["qkv"], 2 * W, W, y=fchain.qkv, ws=fchain.ws, rowmax=fchain.rowmax),
+            "out: quantize V third (separate pass)": lambda: q.quant_act_columns(chain.qkv, 2 * W, W, xq=chain.xq,
+                                                                                 sa=chain.sa),
+            "out: linear on int8 input": lambda: q.qlinear_w8a8_prequant(chain.xq, chain.sa, *packed["o"],
+                                                                         y=chain.h1, residual=h),
+            "out: fused (quantizes while staging)": lambda: q.qlinear_w8a8_fused(
+                fchain.qkv, 2 * W, W, fchain.rowmax, *packed["o"], y=fchain.h1, residual=h),
+        }
+        fusion = {"us": {k: round(graph_us(torch, fn), 2) for k, fn in parts.items()},
+                  "chain_us": {"separate pass": round(graph_us(torch, lambda: chain.run(h)), 2),
+                               "fused out-projection": round(graph_us(torch, lambda: fchain.run(h)), 2)},
+                  "note": "graph-replayed, 10 calls per graph; the chain keeps the separate pass"}
+        chain.run(h)
+        del fchain
+
     copy_us = None
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -819,6 +848,8 @@ def main():
     if copy_us is not None:
         out["copy_calibration"] = {"bytes": 2 * (256 << 20), "us": round(copy_us, 2),
                                    "GB/s": round(2 * (256 << 20) / copy_us / 1e3, 1)}
+    if fusion is not None:
+        out["fused_act_quant_out_link"] = fusion
     if "small_m" in extras:
         out["small_m_w4a16"] = small_m_w4a16(q, torch, dev, x3, w3)
     if "m256" in extras:
