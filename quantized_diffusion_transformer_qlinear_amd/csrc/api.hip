@@ -405,7 +405,9 @@ int aria_qlinear_grouped(int bits, int group, const aria_linear_problem* problem
             d.w = static_cast<const uint8_t*>(p.wq);
             d.s = static_cast<const half_t*>(p.s_f16);
             d.y = static_cast<half_t*>(p.y_f16);
-            make_epi(p.epi, mode, p.M, p.N, p.y_f16, &d.epi);
+            Epi e;
+            make_epi(p.epi, mode, p.M, p.N, p.y_f16, &e);   // validated above
+            d.epi = EpiW{e.bias, e.residual, e.steer_dir, e.steer_alpha, e.gelu};
             d.M = (int)p.M, d.N = (int)p.N, d.K = (int)p.K;
         }
         const int rc = hip_status(launch_skinny_grouped(bits, g, st));

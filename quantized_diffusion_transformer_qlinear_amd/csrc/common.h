@@ -44,14 +44,26 @@ __device__ __forceinline__ float gelu_tanh(float y) {
 }
 
 // Steering strength, read once per thread from device memory (0 if absent).
-__device__ __forceinline__ float load_alpha(const Epi& e) {
+// The terms a weight-only linear of the grouped call takes (no raw
+// accumulators, no row maxima): kept small because the grouped call's
+// problem table travels as the kernel argument.
+struct EpiW {
+    const half_t* bias;
+    const half_t* residual;
+    const float* steer_dir;
+    const float* steer_alpha;
+    int gelu;
+};
+
+template <class E>
+__device__ __forceinline__ float load_alpha(const E& e) {
     return (e.steer_dir && e.steer_alpha) ? __builtin_nontemporal_load(e.steer_alpha) : 0.0f;
 }
 
 // y (the dequantized accumulator) -> + bias -> GELU -> + residual -> + alpha d.
-// `idx` is m * N + n.
-__device__ __forceinline__ float epilogue_apply(float y, int64_t idx, int n, const Epi& e,
-                                                float alpha) {
+// `idx` is m * N + n.  E: Epi or EpiW.
+template <class E>
+__device__ __forceinline__ float epilogue_apply(float y, int64_t idx, int n, const E& e, float alpha) {
     if (e.bias) y += (float)e.bias[n];
     if (e.gelu) y = gelu_tanh(y);
     if (e.residual) y += (float)e.residual[idx];

@@ -107,9 +107,9 @@ __device__ __forceinline__ void skinny_compute(const SkinnyRegs<BITS, MT, CG, NS
 // Sum the four waves' partial tiles in a fixed order and apply the epilogue.
 // `part` is reused, so callers that come back for another tile must pass a
 // barrier first (done here at the end).
-template <int BITS, int MT, int CG>
+template <int BITS, int MT, int CG, class E>
 __device__ __forceinline__ void skinny_finish(float (&part)[4][MT * 16][16 * CG + 1], v4f (&acc)[MT][CG],
-                                              const half_t* S, half_t* Y, int M, int N, const Epi& epi, int n0,
+                                              const half_t* S, half_t* Y, int M, int N, const E& epi, int n0,
                                               int wave, int lane) {
     constexpr int NC = 16 * CG;
     // 16x16 block layout: register r of lane l holds row 4*(l/16) + r, column l%16
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256, kStreamPerCU) void gemm_skinny_stream_kernel(S
     const rsrc_t rw = make_rsrc(P.w, (uint32_t)P.N * rowb);
     const rsrc_t rs = make_rsrc(P.s, (uint32_t)P.N * G * 2);
     const rsrc_t ry = make_rsrc(P.y, (uint32_t)P.M * (uint32_t)P.N * 2);
-    const Epi& e = P.epi;
+    const EpiW& e = P.epi;
     const bool steer = e.steer_dir && e.steer_alpha;
     const rsrc_t rbias = make_rsrc(e.bias, e.bias ? (uint32_t)P.N * 2 : 0u);
     const rsrc_t rres = make_rsrc(e.residual, e.residual ? (uint32_t)P.M * (uint32_t)P.N * 2 : 0u);
@@ -520,8 +520,15 @@ hipError_t launch_skinny_grouped(int bits, SkinnyGroup& g, hipStream_t st) {
         int cus = 0, dev = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
+        // the smallest run length whose workgroups (each problem's runs
+        // rounded up on its own) all fit in one wave of resident workgroups
         const int slots = kStreamPerCU * cus;
-        const int per = (units + slots - 1) / slots;
+        int per = (units + slots - 1) / slots;
+        for (;; per++) {
+            int need = 0;
+            for (int i = 0; i < g.count; i++) need += ((g.p[i].N + kStreamCh - 1) / kStreamCh + per - 1) / per;
+            if (need <= slots) break;
+        }
         int wgs = 0;
         for (int i = 0; i < g.count; i++) {
             g.p[i].first = wgs;

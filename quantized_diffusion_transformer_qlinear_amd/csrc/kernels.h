@@ -57,7 +57,7 @@ struct SkinnyProblem {
     const uint8_t* w;
     const half_t* s;
     half_t* y;
-    Epi epi;
+    EpiW epi;
     int M, N, K;
     int first;  // first workgroup of this problem (set by the launcher)
 };
@@ -65,6 +65,8 @@ struct SkinnyGroup {
     SkinnyProblem p[kSkinnyGroupMax];
     int count;
 };
+// the problem table is the kernel argument: keep it within 4 KB
+static_assert(sizeof(SkinnyGroup) <= 4096, "grouped problem table exceeds 4 KB of kernel arguments");
 hipError_t launch_skinny_grouped(int bits, SkinnyGroup& g, hipStream_t st);
 
 }  // namespace aria
