@@ -44,9 +44,11 @@
  *       W   fp16 [K][N]            unpacked weights (input of aria_qpack only)
  *       Wq  int8 [N][K]            8-bit weights, row n contiguous along K
  *       s_w fp16 [N]               8-bit weight scales
- *       Wq4 uint8 [N][K/2]         4-bit weights: byte j of row n holds
- *                                  k = 2j in its low nibble, k = 2j+1 in its
- *                                  high nibble, two's complement
+ *       Wq4 uint8 [N][K/2]         4-bit weights, two's complement nibbles:
+ *                                  the little-endian 32-bit word d of row n
+ *                                  (bytes 4d .. 4d+3) holds k = 8d .. 8d+7,
+ *                                  k = 8d+2i in bits 4i .. 4i+3 and
+ *                                  k = 8d+2i+1 in bits 16+4i .. 16+4i+3
  *       s_g fp16 [N][K/32]         4-bit group scales, group g = k in [32g, 32g+32)
  *       Wt  fp16 [N][K]            fp16 weights (the unquantized rung), row n = column n of W
  *       Y   fp16 [M][N]            output

@@ -21,7 +21,7 @@
  *        instead of adding to it.
  * The pages state the goal, not the formulas.  The formulas below are the plain
  * readings listed in the design notes (fp16 scales, absmax/qmax, round half to
- * even, qmax 127 / 7, group 32 along K, low nibble = even k, epilogue order
+ * even, qmax 127 / 7, group 32 along K, the 4-bit word layout below, epilogue order
  * scale -> bias -> GELU(tanh) -> residual -> alpha*d).
  *
  * Arithmetic: integers exactly in int64 (asserted to fit int32 where the GPU
@@ -137,10 +137,26 @@ int or_quant_sym(const uint16_t* v, int64_t L, int64_t stride, int qmax,
 /* a1  Weight packing.  W is fp16 [K][N] row-major (K inputs, N outputs).     */
 /* q8: per output channel n, quantize the column W[:, n] with qmax 127;      */
 /*     Wq int8 [N][K] (row n contiguous along K), s fp16 [N].                 */
-/* q4: per (n, group g) quantize W[gG .. gG+G), n] with qmax 7; pack two     */
-/*     two's-complement nibbles per byte, low nibble = even k:                */
-/*     Wq4[n][j] = (q[2j] & 0xF) | ((q[2j+1] & 0xF) << 4); s fp16 [N][K/G].   */
+/* q4: per (n, group g) quantize W[gG .. gG+G), n] with qmax 7; s fp16       */
+/*     [N][K/G].  Row n of Wq4 is K/2 bytes: the codes of each run of eight   */
+/*     consecutive k (k = 8d .. 8d+7) form its little-endian 32-bit word d    */
+/*     (bytes 4d .. 4d+3), even k = 8d+2i in bits 4i .. 4i+3 and odd          */
+/*     k = 8d+2i+1 in bits 16+4i .. 16+4i+3 (i = 0..3), as two's-complement   */
+/*     nibbles.  (The byte layout is the library's own choice; with the even  */
+/*     codes in one half-word and the odd ones in the other, one mask of a    */
+/*     word yields the fp16 pair of two adjacent k.)                          */
 /* ------------------------------------------------------------------------- */
+
+/* Bit position of code k within its row's word k / 8 (layout above). */
+static int or_q4_bit(int64_t k) { return (int)((k % 2) * 16 + ((k % 8) / 2) * 4); }
+
+/* The nibble of code k in row q4r (K/2 bytes), two's complement -> int. */
+static int or_q4_get(const uint8_t* q4r, int64_t k)
+{
+    const int bit = or_q4_bit(k);
+    const int nib = (q4r[4 * (k / 8) + bit / 8] >> (bit % 8)) & 0xF;
+    return nib >= 8 ? nib - 16 : nib;
+}
 int or_qpack8(const uint16_t* w, int64_t K, int64_t N, int8_t* q, uint16_t* s)
 {
     if (!w || !q || !s || K <= 0 || N <= 0) return -1;
@@ -153,7 +169,7 @@ int or_qpack8(const uint16_t* w, int64_t K, int64_t N, int8_t* q, uint16_t* s)
 
 int or_qpack4(const uint16_t* w, int64_t K, int64_t N, int64_t group, uint8_t* q4, uint16_t* s)
 {
-    if (!w || !q4 || !s || K <= 0 || N <= 0 || group <= 0 || (group % 2) || K % group) return -1;
+    if (!w || !q4 || !s || K <= 0 || N <= 0 || group <= 0 || (group % 2) || K % group || K % 8) return -1;
     int64_t G = K / group;
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(|:bad)
@@ -162,8 +178,12 @@ int or_qpack4(const uint16_t* w, int64_t K, int64_t N, int64_t group, uint8_t* q
         if (!qcol) { bad = 1; continue; }
         for (int64_t g = 0; g < G; g++)
             bad |= (or_quant_sym(w + g * group * N + n, group, N, 7, qcol + g * group, s + n * G + g) != 0);
-        for (int64_t j = 0; j < K / 2; j++)
-            q4[n * (K / 2) + j] = (uint8_t)((qcol[2 * j] & 0xF) | ((qcol[2 * j + 1] & 0xF) << 4));
+        uint8_t* row = q4 + n * (K / 2);
+        memset(row, 0, (size_t)(K / 2));
+        for (int64_t k = 0; k < K; k++) {
+            const int bit = or_q4_bit(k);
+            row[4 * (k / 8) + bit / 8] |= (uint8_t)((qcol[k] & 0xF) << (bit % 8));
+        }
         free(qcol);
     }
     return bad ? -2 : 0;
@@ -172,13 +192,9 @@ int or_qpack4(const uint16_t* w, int64_t K, int64_t N, int64_t group, uint8_t* q
 /* Inverse of the nibble packing (two's complement 4-bit -> int8). */
 int or_unpack4(const uint8_t* q4, int64_t K, int64_t N, int8_t* q)
 {
-    if (!q4 || !q || K <= 0 || N <= 0 || (K % 2)) return -1;
+    if (!q4 || !q || K <= 0 || N <= 0 || (K % 8)) return -1;
     for (int64_t n = 0; n < N; n++)
-        for (int64_t j = 0; j < K / 2; j++) {
-            int lo = q4[n * (K / 2) + j] & 0xF, hi = (q4[n * (K / 2) + j] >> 4) & 0xF;
-            q[n * K + 2 * j] = (int8_t)(lo >= 8 ? lo - 16 : lo);
-            q[n * K + 2 * j + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
-        }
+        for (int64_t k = 0; k < K; k++) q[n * K + k] = (int8_t)or_q4_get(q4 + n * (K / 2), k);
     return 0;
 }
 
@@ -239,7 +255,7 @@ int or_ref_w8a16(const uint16_t* x, const int8_t* wq, const uint16_t* sw,
 int or_ref_w4a16(const uint16_t* x, const uint8_t* wq4, const uint16_t* sg, int64_t group,
                  int64_t M, int64_t N, int64_t K, double* r)
 {
-    if (!x || !wq4 || !sg || !r || M <= 0 || N <= 0 || K <= 0 || group <= 0 || K % group || (K % 2))
+    if (!x || !wq4 || !sg || !r || M <= 0 || N <= 0 || K <= 0 || group <= 0 || K % group || (K % 8))
         return -1;
     int64_t G = K / group;
     /* dequantized weights, computed once: wd[n][k] = q * s (exact in fp64) */
@@ -248,8 +264,7 @@ int or_ref_w4a16(const uint16_t* x, const uint8_t* wq4, const uint16_t* sg, int6
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; n++)
         for (int64_t k = 0; k < K; k++) {
-            int nib = (wq4[n * (K / 2) + k / 2] >> ((k % 2) * 4)) & 0xF;
-            int qv = nib >= 8 ? nib - 16 : nib;
+            const int qv = or_q4_get(wq4 + n * (K / 2), k);
             wd[n * K + k] = (double)qv * or_f16_to_f64(sg[n * G + k / group]);
         }
 #pragma omp parallel for schedule(static)

@@ -28,31 +28,32 @@ __device__ __forceinline__ void dec8(v4i w, v4i& lo, v4i& hi) {
     hi = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
 }
 
-// 8 ND nibbles (ND dwords; even k in the low nibble) -> 8 ND fp16 values
-// fp16(q * s).  For the pair k = 2j, 2j+1 (byte j of a dword) a byte permute
-// copies byte j into bytes 0 and 2; one three-input bit operation then keeps
-// the low nibble in the low half and the high nibble at bits 4-7 of the high
-// half, flips each nibble's top bit ((n ^ 8) = q + 8 = u) and sets the two
-// exponents, so the low half reads 1024 + u (0x6400 | u: unit steps) and the
-// high half 64 + u (0x5400 | u << 4: exponent 6, where mantissa bit 4 is
-// worth 1).  One packed subtract of (1032, 72) leaves q exactly, one packed
-// multiply by the group scale rounds once.  Four VALU ops per pair.
+// 8 ND nibbles (ND dwords) -> 8 ND fp16 values fp16(q * s).  Dword d holds
+// k = 8d .. 8d + 7: the even k in the four nibbles of its low half-word, the
+// odd k in those of its high half-word.  So one three-input bit operation on
+// the dword keeps the pair (k, k + 1) of one nibble position from both halves,
+// flips each nibble's top bit ((n ^ 8) = q + 8 = u) and sets the exponents:
+// nibble 0 (bits 0-3 / 16-19) reads 1024 + u (0x6400 | u: unit steps), nibble
+// 1 (bits 4-7 / 20-23) reads 64 + u (0x5400 | u << 4: exponent 6, where
+// mantissa bit 4 is worth 1); nibbles 2 and 3 the same after an 8-bit shift.
+// One packed subtract of the offset leaves q exactly, one packed multiply by
+// the group scale rounds once.  13 VALU ops per 8 values.
 template <int ND = 4>
 __device__ __forceinline__ void dec4(v4i w, v2h sc, v4i out[ND]) {
-    const v2h bias = {(half_t)1032.0f, (half_t)72.0f};
+    const v2h b0 = {(half_t)1032.0f, (half_t)1032.0f}, b1 = {(half_t)72.0f, (half_t)72.0f};
 #pragma unroll
     for (int d = 0; d < ND; d++) {
-        const u32 u = (u32)w[d];
-        u32 o[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            // selector bytes j, 0x0C (zero), j, 0x0C: the dword reads b_j, 0, b_j, 0
-            const u32 b = __builtin_amdgcn_perm(0u, u, 0x0C000C00u | (u32)j | ((u32)j << 16));
-            const u32 p = (b & 0x00F0000Fu) ^ 0x54806408u;
-            v2h h = (__builtin_bit_cast(v2h, p) - bias) * sc;
-            o[j] = __builtin_bit_cast(u32, h);
-        }
-        out[d] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        const u32 u = (u32)w[d], u8 = u >> 8;
+        const u32 p0 = (u & 0x000F000Fu) ^ 0x64086408u;    // k 8d + 0, 1
+        const u32 p1 = (u & 0x00F000F0u) ^ 0x54805480u;    // k 8d + 2, 3
+        const u32 p2 = (u8 & 0x000F000Fu) ^ 0x64086408u;   // k 8d + 4, 5
+        const u32 p3 = (u8 & 0x00F000F0u) ^ 0x54805480u;   // k 8d + 6, 7
+        const v2h h0 = (__builtin_bit_cast(v2h, p0) - b0) * sc;
+        const v2h h1 = (__builtin_bit_cast(v2h, p1) - b1) * sc;
+        const v2h h2 = (__builtin_bit_cast(v2h, p2) - b0) * sc;
+        const v2h h3 = (__builtin_bit_cast(v2h, p3) - b1) * sc;
+        out[d] = v4i{(int)__builtin_bit_cast(u32, h0), (int)__builtin_bit_cast(u32, h1), (int)__builtin_bit_cast(u32, h2),
+                     (int)__builtin_bit_cast(u32, h3)};
     }
 }
 template <int ND = 4>

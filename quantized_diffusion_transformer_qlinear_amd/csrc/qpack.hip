@@ -105,12 +105,20 @@ __global__ __launch_bounds__(256) void qpack4_kernel(const half_t* __restrict__ 
             for (int i = 0; i < 32; i++) a = fmaxf(a, fabsf((float)tile[g * 32 + i][cn]));
             half_t sh = (half_t)(a / 7.0f);
             const float sc = (float)sh;
-            union { uint8_t b[16]; v4i v; } out;
+            // word d of the group's 16 bytes holds k = 8d .. 8d + 7: the even
+            // k in the nibbles of its low half-word, the odd k in its high one
+            union { uint32_t w[4]; v4i v; } out;
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                int lo = quant_one((float)tile[g * 32 + 2 * j][cn], sc, 7.0f);
-                int hi = quant_one((float)tile[g * 32 + 2 * j + 1][cn], sc, 7.0f);
-                out.b[j] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+            for (int d = 0; d < 4; d++) {
+                uint32_t wd = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int ev = quant_one((float)tile[g * 32 + 8 * d + 2 * i][cn], sc, 7.0f);
+                    const int od = quant_one((float)tile[g * 32 + 8 * d + 2 * i + 1][cn], sc, 7.0f);
+                    wd |= ((uint32_t)ev & 0xFu) << (4 * i);
+                    wd |= ((uint32_t)od & 0xFu) << (16 + 4 * i);
+                }
+                out.w[d] = wd;
             }
             *reinterpret_cast<v4i*>(q4 + (n0 + cn) * (K / 2) + kb / 2) = out.v;
             s[(n0 + cn) * G + kb / 32] = sh;

@@ -82,3 +82,21 @@ def sign_extend4(nib: np.ndarray) -> np.ndarray:
     """4-bit two's complement -> int, via the xor-8 identity."""
     nib = np.asarray(nib, np.int64) & 0xF
     return (nib ^ 8) - 8
+
+
+def unpack4_words(q4: np.ndarray) -> np.ndarray:
+    """Packed 4-bit rows uint8 [N][K/2] -> int64 [N][K], read word by word: the
+    little-endian 32-bit word d of a row holds k = 8d .. 8d+7, the even k
+    (8d + 2i) in the four nibbles of its low half-word and the odd k
+    (8d + 2i + 1) in those of its high half-word, nibble i at bits 4i."""
+    b = np.asarray(q4, np.int64)
+    N, KB = b.shape
+    words = b.reshape(N, KB // 4, 4)
+    lo16 = words[:, :, 0] | (words[:, :, 1] << 8)
+    hi16 = words[:, :, 2] | (words[:, :, 3] << 8)
+    out = np.empty((N, KB // 4, 8), np.int64)
+    for i in range(4):
+        out[:, :, 2 * i] = sign_extend4(lo16 >> (4 * i))
+        out[:, :, 2 * i + 1] = sign_extend4(hi16 >> (4 * i))
+    return out.reshape(N, 2 * KB)
+

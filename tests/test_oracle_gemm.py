@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.exact import sign_extend4
+from tests.exact import unpack4_words
 
 
 def test_k1_all_pairs():
@@ -56,9 +56,7 @@ def test_w4a16_vs_blas():
     q4 = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
     s4 = (rng.random((N, K // 32)) * 1e-2).astype(np.float16)
     r = oracle.ref_w4a16(x, q4, s4, 32)
-    wd = np.empty((N, K))
-    wd[:, 0::2] = sign_extend4(q4)
-    wd[:, 1::2] = sign_extend4(q4 >> 4)
+    wd = unpack4_words(q4).astype(np.float64)
     wd *= np.repeat(s4.astype(np.float64), 32, axis=1)
     ref = x.astype(np.float64) @ wd.T
     assert np.max(np.abs(r - ref)) <= 1e-12 * np.max(np.abs(ref))

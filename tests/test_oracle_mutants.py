@@ -34,12 +34,13 @@ MUTANTS = {
     "scale_qmax_plus_one": ("or_f64_to_f16(a / (double)qmax)", "or_f64_to_f16(a / (double)(qmax + 1))"),
     "scale_not_stored": ("double r = or_rne(or_f16_to_f64(v[i * stride]) / sd);",
                          "double r = or_rne(or_f16_to_f64(v[i * stride]) / (a / qmax));"),
-    "nibble_order": ("(uint8_t)((qcol[2 * j] & 0xF) | ((qcol[2 * j + 1] & 0xF) << 4))",
-                     "(uint8_t)((qcol[2 * j + 1] & 0xF) | ((qcol[2 * j] & 0xF) << 4))"),
+    "q4_sequential_nibbles": ("return (int)((k % 2) * 16 + ((k % 8) / 2) * 4);", "return (int)((k % 8) * 4);"),
+    "q4_halves_swapped": ("return (int)((k % 2) * 16 + ((k % 8) / 2) * 4);",
+                          "return (int)((1 - k % 2) * 16 + ((k % 8) / 2) * 4);"),
     "group_column_stride": ("or_quant_sym(w + g * group * N + n, group, N,", "or_quant_sym(w + g * group + n, group, N,"),
     "gemm_drops_last_k": ("for (int64_t k = 0; k < K; k++) t += (int64_t)xq", "for (int64_t k = 0; k + 1 < K; k++) t += (int64_t)xq"),
     "w8a16_no_scale": ("r[m * N + n] = or_f16_to_f64(sw[n]) * t;", "r[m * N + n] = t;"),
-    "w4a16_no_sign_extend": ("int qv = nib >= 8 ? nib - 16 : nib;", "int qv = nib;"),
+    "w4a16_no_sign_extend": ("return nib >= 8 ? nib - 16 : nib;", "return nib;"),
     "w4a16_group_index": ("sg[n * G + k / group]", "sg[n * G + k % G]"),
     "w8a8_drop_act_scale": ("(double)acc[m * N + n] * or_f16_to_f64(sa[m]) * or_f16_to_f64(sw[n])",
                             "(double)acc[m * N + n] * or_f16_to_f64(sw[n])"),
