@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -40,11 +41,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_dit_qlinear_m2048.txt
 KERNEL_SOURCES = ["common.h", "decode.h", "rowops.h", "gemm_tiled.hip", "gemm_skinny.hip", "actquant.hip"]
 
 
+def code_only(text: str) -> str:
+    """C++ source without comments or blank lines (what the compiler sees)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_hash() -> str:
+    """Identifies the kernels' code (comments excluded), so that counter
+    readings taken on other code are not reported."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "quantized_diffusion_transformer_qlinear_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_diffusion_transformer_qlinear_amd", "csrc", f)) as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -26,9 +26,9 @@
 // then complete in LDS, and its first fragments are read while the last
 // sub-step's MFMAs run (a barrier at the end of the K-step left every wave
 // waiting on those reads with nothing to issue).  Packed weights are decoded
-// in registers (decode.h: fp16 patterns 0x6400 | u and, for the high nibble,
-// 0x5400 | u << 4, minus their offsets), two values per packed-half
-// instruction.  The epilogue stages the accumulators through LDS and writes
+// in registers (decode.h: fp16 patterns 0x6400 | u and, for the codes left in
+// mantissa bits 4-7, 0x5400 | u << 4, minus their offsets), two values per
+// packed-half instruction.  The epilogue stages the accumulators through LDS and writes
 // 16-byte rows of fp16 with non-temporal stores.
 #include <type_traits>
 

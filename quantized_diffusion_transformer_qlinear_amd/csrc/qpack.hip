@@ -5,8 +5,11 @@
 // releases the fp16 copy.  Symmetric absmax quantization with an fp16 scale:
 //   s = fp16_RNE(max|v| / qmax),  q = clamp(RNE(v / s), -qmax, qmax),  s == 0 -> q = 0
 // q8 : per output channel n over all K, qmax 127 -> Wq int8 [N][K], s [N]
-// q4 : per (n, group of 32 k), qmax 7 -> two's-complement nibbles, even k in
-//      the low nibble, Wq4 uint8 [N][K/2], s [N][K/32]
+// q4 : per (n, group of 32 k), qmax 7 -> two's-complement nibbles,
+//      Wq4 uint8 [N][K/2], s [N][K/32]: each 32-bit word of a row holds eight
+//      consecutive k, the even ones in the nibbles of its low half-word and
+//      the odd ones in those of its high half-word (decode.h reads a (k, k+1)
+//      pair out of the word with one mask)
 //
 // Bit-exactness with the fp64 definition: the scale is formed as an IEEE fp32
 // quotient rounded to fp16 (equal to rounding the exact quotient, because fp32
