@@ -467,13 +467,42 @@ namespace {
 template <int BITS>
 constexpr int kNS = BITS == 8 ? 6 : BITS == 4 ? 3 : 12;
 
-template <int BITS, int MT>
-hipError_t launch_skinny_mt(const half_t* x, const uint8_t* wq, const half_t* s, half_t* y, int M, int N, int K,
+// Compute units of the current device (queried once).
+int skinny_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, n = 0;
+        cus = hipGetDevice(&dev) == hipSuccess &&
+                      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                  ? n
+                  : 256;
+    }
+    return cus;
+}
+
+template <int BITS, int MT, int CG>
+hipError_t launch_skinny_cg(const half_t* x, const uint8_t* wq, const half_t* s, half_t* y, int M, int N, int K,
                             const Epi& epi, hipStream_t st) {
-    constexpr int CG = 1;
     dim3 grid((N + 16 * CG - 1) / (16 * CG)), block(256);
     hipLaunchKernelGGL((gemm_skinny_kernel<BITS, MT, CG, kNS<BITS>>), grid, block, 0, st, x, wq, s, y, M, N, K, epi);
     return hipGetLastError();
+}
+
+// One workgroup per 16 output channels, or per 32 where that halves a grid of
+// one to two workgroups per CU at M > 8: every workgroup reads all of X (for
+// 16 rows four times the bytes of its 4-bit weights), so fewer workgroups
+// read less of it.  Measured at K = 1536, one dependent launch per layer:
+// M = 16, N = 4608 / 6144 / 8192: W4A16 6.5-6.6 -> 5.9-6.1 us, W8A16
+// 6.7-7.0 -> 6.0-6.7 us; at M = 4 (X rows past M read nothing) it does not
+// pay, nor beyond two workgroups per CU.  The sums are the same either way.
+template <int BITS, int MT>
+hipError_t launch_skinny_mt(const half_t* x, const uint8_t* wq, const half_t* s, half_t* y, int M, int N, int K,
+                            const Epi& epi, hipStream_t st) {
+    if constexpr (BITS != 16 && MT == 1) {
+        const int cus = skinny_cus();
+        if (M > 8 && N > 16 * cus && N <= 32 * cus) return launch_skinny_cg<BITS, MT, 2>(x, wq, s, y, M, N, K, epi, st);
+    }
+    return launch_skinny_cg<BITS, MT, 1>(x, wq, s, y, M, N, K, epi, st);
 }
 
 template <int BITS>

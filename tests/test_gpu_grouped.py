@@ -89,6 +89,22 @@ def test_grouped_more_than_one_launch(q):
         assert_close(host(outs[i]), _oracle(4, x, w, e), f"grouped #{i} {shapes[i]}")
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N,epi", [(9, 512, 4104, ("bias", "gelu", "residual", "steer")),
+                                       (16, 1536, 6144, ()), (16, 256, 8192, ("residual",))])
+def test_single_call_two_groups(q, bits, M, K, N, epi):
+    """Widths where the single call at M > 8 gives each workgroup two 16-channel
+    groups (one to two workgroups per CU on a 256-CU device; N = 4104 leaves
+    the last workgroup half a group): within tolerance of the oracle and
+    bit-identical to the grouped call, whose workgroups take more groups."""
+    x, w, e, p = _problem(q, bits, M, K, N, 4100 + M + bits, epi)
+    log(f"single w{bits}a16 {M}x{K}x{N} {epi}")
+    y = _single(q, bits, p)
+    assert_close(host(y), _oracle(bits, x, w, e), f"single w{bits}a16 {M}x{K}x{N}")
+    g = q.qlinear_grouped(bits, [p])[0]
+    assert host(y).tobytes() == host(g).tobytes(), "single and grouped calls differ"
+
+
 def test_grouped_in_place_residual(q):
     x, w, e, p = _problem(q, 4, 24, 320, 96, 77, ("residual",))
     h = p["residual"]
