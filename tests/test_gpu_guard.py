@@ -48,7 +48,7 @@ def _inputs(M, K, N, seed):
 
 
 @pytest.mark.parametrize("mode", ["w8a8", "w8a16", "w4a16", "w16a16"])
-@pytest.mark.parametrize("M,K,N", [(300, 352, 460), (300, 416, 520), (37, 352, 460), (5, 96, 520)])
+@pytest.mark.parametrize("M,K,N", [(300, 352, 460), (300, 416, 520), (37, 352, 460), (5, 96, 520), (12, 256, 4104)])
 def test_output_guard_bands(q, mode, M, K, N):
     import torch
     log(f"guard {mode} {M}x{K}x{N}")
