@@ -10,7 +10,7 @@
 //   W16A16: acc = sum_k X[m][k] * Wt[n][k]  (fp32);  y = acc
 // then y -> + bias -> GELU -> + residual -> + alpha d -> fp16.
 //
-// Design (gfx950): a workgroup of WM x WN waves (4, 8, 12 or 16; a 4-wave tile
+// Design (gfx950): a workgroup of WM x WN waves (4, 6, 8, 12 or 16; a 4-wave tile
 // may also run as two such groups that split the K-steps) owns a BM x BN
 // output tile; each wave owns (BM/WM) x (BN/WN) as 32x32 blocks on the matrix cores
 // (v_mfma_i32_32x32x32_i8 or v_mfma_f32_32x32x16_f16).  Both operands live in
@@ -129,12 +129,13 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     const int G = K / 32;
 
     // per-thread chunk coordinates (fixed across K-steps)
-    // 4-wave tiles (two workgroups per CU) keep the next-but-one tile in a
-    // second register set, so a load has a whole K-step to land; so does the
-    // 12-wave W8A16 tile (168 VGPRs, +5 % measured).  Elsewhere the second
-    // set cost 1-6 % (8-wave tiles) or spilled (12-wave W8A8, W4A16), and
-    // the extra waves per SIMD hide the latency instead.
-    constexpr int NSET = WM * WN == 4 || (WM * WN == 12 && MODE == 1) ? 2 : 1;
+    // 4- and 6-wave tiles keep the next-but-one tile in a second register
+    // set, so a load has a whole K-step to land (6 waves, 64x96 at M = 256:
+    // W8A16 13.7 -> 11.7 us, W8A8 -5 %); so does the 12-wave W8A16 tile
+    // (168 VGPRs, +5 % measured).  Elsewhere the second set cost 1-6 %
+    // (8-wave tiles) or spilled (12-wave W8A8, W4A16), and the extra waves
+    // per SIMD hide the latency instead.
+    constexpr int NSET = WM * WN == 4 || WM * WN == 6 || (WM * WN == 12 && MODE == 1) ? 2 : 1;
     // PIN: every part's loads and stores stay in their sub-step (a scheduling
     // barrier after each), and every wave issues the same loads (see load_a),
     // so the compiler's waits give each load a whole K-step to land; without
@@ -633,10 +634,14 @@ constexpr TileCfg kTiles[] = {
     // +12-16 % (+20 % at K = 6144 and 8192), W16A16 +1-2 %, W8A8 -2-5 %
     {64, 192, 2, 2, 2, {2218.f, 1600.f, 1322.f, 1420.f}}, {128, 128, 2, 2, 2, {2629.f, 2116.f, 1814.f, 1932.f}},
     // the 128x64 and 64x128 tiles with two K groups, measured at M = 256,
-    // 1536 -> 6144: W8A16 +10 % / +19 % over one group; W4A16 no gain, so
-    // they are priced just below the one-group entries there (and for the
-    // modes not measured)
-    {128, 64, 2, 2, 2, {2200.f, 1468.f, 1210.f, 1340.f}}, {64, 128, 2, 2, 2, {2260.f, 1535.f, 1095.f, 1330.f}}};
+    // 1536 -> 6144 over one group: W8A16 +10 % / +19 %, W4A16 +15 % / +16 %;
+    // W8A8 and W16A16 no gain, so priced just below the one-group entries
+    {128, 64, 2, 2, 2, {2200.f, 1468.f, 1404.f, 1340.f}}, {64, 128, 2, 2, 2, {2260.f, 1535.f, 1284.f, 1330.f}},
+    // 6 waves, 64x96: 256 tiles at M = 256, N = 6144 (one per CU where the
+    // 128x64 tile leaves 64 CUs idle); fitted at that shape against the
+    // 128x64 tile: W8A8 12.5 -> 11.4 us, W8A16 13.3 -> 11.8, W4A16 14.1 ->
+    // 13.4, W16A16 15.2 -> 13.7
+    {64, 96, 2, 3, 1, {1832.f, 1125.f, 962.f, 1124.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -704,6 +709,7 @@ hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const 
     ARIA_TILE(128, 256, 2, 4, 1) ARIA_TILE(128, 192, 2, 2, 1) ARIA_TILE(128, 128, 2, 2, 1) ARIA_TILE(64, 192, 2, 2, 1)
     ARIA_TILE(128, 64, 2, 2, 1) ARIA_TILE(64, 128, 2, 2, 1) ARIA_TILE(64, 64, 2, 2, 1)
     ARIA_TILE(64, 192, 2, 2, 2) ARIA_TILE(128, 128, 2, 2, 2) ARIA_TILE(128, 64, 2, 2, 2) ARIA_TILE(64, 128, 2, 2, 2)
+    ARIA_TILE(64, 96, 2, 3, 1)
 #undef ARIA_TILE
     return hipErrorInvalidValue;
 }

@@ -52,7 +52,8 @@ def test_producer_rowmax(q, M, K, W3, c0, nc):
 
 
 @pytest.mark.parametrize("M,K,N,epi", [(2048, 1536, 1536, "residual"), (300, 256, 520, "bias_gelu"),
-                                       (77, 64, 256, None), (513, 512, 1536, "steer"), (64, 1536, 4608, None)])
+                                       (77, 64, 256, None), (513, 512, 1536, "steer"), (64, 1536, 4608, None),
+                                       (256, 1536, 6144, "bias_gelu")])
 def test_consumer_matches_quantize_then_linear(q, M, K, N, epi):
     import torch
     log(f"fused consumer {M}x{K}x{N} epi={epi}")
