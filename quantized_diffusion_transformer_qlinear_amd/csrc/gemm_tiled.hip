@@ -641,7 +641,15 @@ constexpr TileCfg kTiles[] = {
     // 128x64 tile leaves 64 CUs idle); fitted at that shape against the
     // 128x64 tile: W8A8 12.5 -> 11.4 us, W8A16 13.3 -> 11.8, W4A16 14.1 ->
     // 13.4, W16A16 15.2 -> 13.7
-    {64, 96, 2, 3, 1, {1832.f, 1125.f, 962.f, 1124.f}}};
+    {64, 96, 2, 3, 1, {1832.f, 1125.f, 962.f, 1124.f}},
+    // 6 waves of 64x32, 128x96: 256 tiles for a 2048 x 1536 output, with
+    // (128 + 96) K operand rows per tile where 64x192 streams (64 + 192);
+    // measured at M = 2048, N = 1536 against the picks before it (act-quant
+    // included for W8A8): W8A8 K = 1536 17.8 -> 16.8 us, K = 6144 43.0 ->
+    // 39.7; W8A16 17.8 -> 15.8 and 52.1 -> 51.9; W4A16 -7 % at K = 1536 but
+    // +5 % at K = 6144, so it is priced below the 128x128 two-group tile
+    // there (W16A16 not measured, priced below 64x192)
+    {128, 96, 2, 3, 1, {2491.f, 1650.f, 1300.f, 1300.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -709,7 +717,7 @@ hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const 
     ARIA_TILE(128, 256, 2, 4, 1) ARIA_TILE(128, 192, 2, 2, 1) ARIA_TILE(128, 128, 2, 2, 1) ARIA_TILE(64, 192, 2, 2, 1)
     ARIA_TILE(128, 64, 2, 2, 1) ARIA_TILE(64, 128, 2, 2, 1) ARIA_TILE(64, 64, 2, 2, 1)
     ARIA_TILE(64, 192, 2, 2, 2) ARIA_TILE(128, 128, 2, 2, 2) ARIA_TILE(128, 64, 2, 2, 2) ARIA_TILE(64, 128, 2, 2, 2)
-    ARIA_TILE(64, 96, 2, 3, 1)
+    ARIA_TILE(64, 96, 2, 3, 1) ARIA_TILE(128, 96, 2, 3, 1)
 #undef ARIA_TILE
     return hipErrorInvalidValue;
 }
