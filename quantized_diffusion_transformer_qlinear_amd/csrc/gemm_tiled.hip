@@ -649,7 +649,12 @@ constexpr TileCfg kTiles[] = {
     // 39.7; W8A16 17.8 -> 15.8 and 52.1 -> 51.9; W4A16 -7 % at K = 1536 but
     // +5 % at K = 6144, so it is priced below the 128x128 two-group tile
     // there (W16A16 not measured, priced below 64x192)
-    {128, 96, 2, 3, 1, {2491.f, 1650.f, 1300.f, 1300.f}}};
+    {128, 96, 2, 3, 1, {2491.f, 1650.f, 1300.f, 1300.f}},
+    // 8 waves of 64x32, 128x128: measured at M = N = 2048 against the 4-wave
+    // tile, K = 2048: W8A8 22.6 -> 20.8 us, W8A16 23.5 -> 22.2, W4A16 26.2 ->
+    // 25.0; K = 8192: W8A8 the same, W8A16 / W4A16 slower than the two-group
+    // 4-wave tile, which keeps the higher price for those modes
+    {128, 128, 2, 4, 1, {2926.f, 2002.f, 1650.f, 1880.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -717,7 +722,7 @@ hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const 
     ARIA_TILE(128, 256, 2, 4, 1) ARIA_TILE(128, 192, 2, 2, 1) ARIA_TILE(128, 128, 2, 2, 1) ARIA_TILE(64, 192, 2, 2, 1)
     ARIA_TILE(128, 64, 2, 2, 1) ARIA_TILE(64, 128, 2, 2, 1) ARIA_TILE(64, 64, 2, 2, 1)
     ARIA_TILE(64, 192, 2, 2, 2) ARIA_TILE(128, 128, 2, 2, 2) ARIA_TILE(128, 64, 2, 2, 2) ARIA_TILE(64, 128, 2, 2, 2)
-    ARIA_TILE(64, 96, 2, 3, 1) ARIA_TILE(128, 96, 2, 3, 1)
+    ARIA_TILE(64, 96, 2, 3, 1) ARIA_TILE(128, 96, 2, 3, 1) ARIA_TILE(128, 128, 2, 4, 1)
 #undef ARIA_TILE
     return hipErrorInvalidValue;
 }
