@@ -133,7 +133,8 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
     // set, so a load has a whole K-step to land (6 waves, 64x96 at M = 256:
     // W8A16 13.7 -> 11.7 us, W8A8 -5 %); so does the 12-wave W8A16 tile
     // (168 VGPRs, +5 % measured).  Elsewhere the second set cost 1-6 %
-    // (8-wave tiles) or spilled (12-wave W8A8, W4A16), and the extra waves
+    // (8-wave tiles; the 12-wave W4A16 tile, 167 VGPRs: 1-2 %, on the pinned
+    // or the free schedule) or spilled (12-wave W8A8), and the extra waves
     // per SIMD hide the latency instead.
     constexpr int NSET = WM * WN == 4 || WM * WN == 6 || (WM * WN == 12 && MODE == 1) ? 2 : 1;
     // PIN: every part's loads and stores stay in their sub-step (a scheduling
