@@ -186,14 +186,14 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
             // lane of the wave lands near a half-integer, clamp to +-127
             const v8h x = __builtin_bit_cast(v8h, RA[set][i]);
             float f[8], q[8];
-            bool near = false;
+            float dmax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
                 f[e] = (float)x[e] * qrcp[i];
                 q[e] = __builtin_rintf(f[e]);
-                near |= fabsf(f[e] - q[e]) >= 0.5f - 0x1p-15f;
+                dmax = __builtin_fmaxf(dmax, __builtin_fabsf(f[e] - q[e]));
             }
-            if (__builtin_amdgcn_ballot_w64(near) != 0) {
+            if (__builtin_amdgcn_ballot_w64(dmax >= 0.5f - 0x1p-15f) != 0) {
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     const float qf = __builtin_floorf(f[e]) + 0.5f;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(WM * WN * KS * WAVE) void gemm_tiled_kernel(const v
             for (int h = 0; h < 2; h++) {
                 u32 b[4];
 #pragma unroll
-                for (int e = 0; e < 4; e++) b[e] = (u32)(int)fminf(fmaxf(q[4 * h + e], -127.0f), 127.0f);
+                for (int e = 0; e < 4; e++) b[e] = (u32)(int)__builtin_amdgcn_fmed3f(q[4 * h + e], -127.0f, 127.0f);
                 w[h] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u),
                                              __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u), 0x05040100u);
             }

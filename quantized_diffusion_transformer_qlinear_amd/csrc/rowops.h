@@ -55,16 +55,19 @@ __device__ __forceinline__ void quantize_row(const v8h (&v)[CH], int lane, int m
         // the even side.  The tie test runs only for chunks where some lane
         // of the wave is near a half-integer.  Checked on the host against
         // rint(x / s) in fp32 for every fp16 row maximum and every |x| <= it
-        // (1.0e9 pairs, 0 differ).
+        // (1.0e9 pairs, 0 differ).  The near test takes the largest
+        // |f - q| of the lane's 8 values (one max3 per two values instead of
+        // a compare, a select and bit packing per value: the pass is bound
+        // by its VALU work once the row is in registers).
         float f[8], q[8];
-        bool near = false;
+        float dmax = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             f[e] = (float)v[c][e] * rcp;
             q[e] = __builtin_rintf(f[e]);
-            near |= fabsf(f[e] - q[e]) >= 0.5f - 0x1p-15f;
+            dmax = __builtin_fmaxf(dmax, __builtin_fabsf(f[e] - q[e]));
         }
-        if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        if (__builtin_amdgcn_ballot_w64(dmax >= 0.5f - 0x1p-15f) != 0) {
 #pragma unroll
             for (int e = 0; e < 8; e++) {
                 const float xv = (float)v[c][e];
@@ -77,7 +80,9 @@ __device__ __forceinline__ void quantize_row(const v8h (&v)[CH], int lane, int m
         for (int h = 0; h < 2; h++) {
             u32 b[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) b[e] = (u32)(int)fminf(fmaxf(q[4 * h + e], -127.0f), 127.0f);
+            // clamp to +-127 (med3: q is never a signalling NaN, so no
+            // canonicalising max is needed), then the integer code
+            for (int e = 0; e < 4; e++) b[e] = (u32)(int)__builtin_amdgcn_fmed3f(q[4 * h + e], -127.0f, 127.0f);
             // low bytes of the four codes, in order
             w[h] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u),
                                          __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u), 0x05040100u);
