@@ -116,13 +116,14 @@ def test_grouped_and_pack_guard_bands(q):
     for p, ref, (raw, n) in zip(probs, outs, raws):
         assert bands_intact(raw, n, 2)
         assert np.array_equal(host(p["y"]).view(np.uint16), host(ref).view(np.uint16))
-    # packing: the packed weights and scales of a ragged layer
-    K, N = 352, 460
-    w = dev(_inputs(1, K, N, 9)[1])
-    for bits, qshape, qtype, sshape in ((8, (N, K), torch.int8, (N,)), (4, (N, K // 2), torch.uint8, (N, K // 32))):
-        qb, qraw = guarded(torch, qshape, qtype)
-        sb, sraw = guarded(torch, sshape, torch.float16)
-        q0, s0 = q.qpack(bits, w)
-        q.qpack(bits, w, q=qb, s=sb)
-        assert bands_intact(qraw, int(np.prod(qshape)), 1) and bands_intact(sraw, int(np.prod(sshape)), 2)
-        assert np.array_equal(host(qb), host(q0)) and np.array_equal(host(sb).view(np.uint16), host(s0).view(np.uint16))
+    # packing: the packed weights and scales of ragged layers (N % 8 != 0 and
+    # N % 8 == 0 take different kernels)
+    for K, N in ((352, 460), (352, 456)):
+        w = dev(_inputs(1, K, N, 9)[1])
+        for bits, qshape, qtype, sshape in ((8, (N, K), torch.int8, (N,)), (4, (N, K // 2), torch.uint8, (N, K // 32))):
+            qb, qraw = guarded(torch, qshape, qtype)
+            sb, sraw = guarded(torch, sshape, torch.float16)
+            q0, s0 = q.qpack(bits, w)
+            q.qpack(bits, w, q=qb, s=sb)
+            assert bands_intact(qraw, int(np.prod(qshape)), 1) and bands_intact(sraw, int(np.prod(sshape)), 2)
+            assert np.array_equal(host(qb), host(q0)) and np.array_equal(host(sb).view(np.uint16), host(s0).view(np.uint16))

@@ -31,7 +31,11 @@ def _pack_both(q, w, bits):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("K,N", [(32, 1), (64, 3), (96, 65), (160, 130), (256, 64), (544, 97)])
+# N % 8 == 0 takes the 16-byte tiled kernels, any other N the channel-strip
+# ones: both with K tails past a tile (K % 128, K % 64 != 0) and partial
+# channel blocks
+@pytest.mark.parametrize("K,N", [(32, 1), (64, 3), (96, 65), (160, 130), (256, 64), (544, 97),
+                                 (32, 8), (96, 72), (160, 136), (544, 200), (1056, 24)])
 def test_pack_ragged(q, bits, K, N):
     log(f"qpack{bits} K={K} N={N}")
     rng = np.random.default_rng(K * 1000 + N)
@@ -43,9 +47,12 @@ def test_pack_ragged(q, bits, K, N):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-def test_pack_fp16_grid(q, bits):
+@pytest.mark.parametrize("mult8", [True, False])
+def test_pack_fp16_grid(q, bits, mult8):
     """Every finite fp16 value appears as a weight, under many scales (columns
-    with different absmax, including subnormal scales and exact ties)."""
+    with different absmax, including subnormal scales and exact ties); with a
+    channel count that is a multiple of 8 (16-byte tiled kernels) and one that
+    is not."""
     vals = FINITE.view(np.float16)
     K = 1024
     cols = []
@@ -58,6 +65,8 @@ def test_pack_fp16_grid(q, bits):
             c[:chunk.size] = chunk
             c[-1] = a                  # absmax of the channel (and of its last group)
             cols.append(c)
+    while (len(cols) % 8 == 0) != mult8:
+        cols.append(np.zeros(K, np.float16))
     w = np.stack(cols, axis=1)
     log(f"qpack{bits} grid K={K} N={w.shape[1]}")
     _pack_both(q, w, bits)
