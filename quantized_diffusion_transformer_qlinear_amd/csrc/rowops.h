@@ -9,10 +9,19 @@
 
 namespace aria {
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
-    return v;
+// The largest of the wave's 64 values (non-negative integers, e.g. fp16
+// magnitude bits), wave-uniform: DPP steps inside each row of 16 lanes (quad
+// swaps, then the half-row and row mirrors), then the four row results
+// through scalar registers.  Cheaper in latency than a chain of six lane
+// shuffles through LDS.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // lanes xor 1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // lanes xor 2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // half-row mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -38,7 +47,8 @@ __device__ __forceinline__ void quantize_row(const v8h (&v)[CH], int lane, int m
 #pragma unroll
         for (int d = 0; d < 4; d++) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(v2us, w[d] & 0x7FFF7FFFu));
     }
-    const float a = wave_max((float)__builtin_bit_cast(half_t, mx[0] > mx[1] ? mx[0] : mx[1]));
+    const uint32_t amax = wave_max_u32(mx[0] > mx[1] ? mx[0] : mx[1]);
+    const float a = (float)__builtin_bit_cast(half_t, (uint16_t)amax);
     const half_t sh = (half_t)(a / 127.0f);
     const float s = (float)sh;
     const float sdiv = s == 0.0f ? 1.0f : s;  // an all-zero row quantizes to zeros either way
@@ -63,7 +73,10 @@ __device__ __forceinline__ void quantize_row(const v8h (&v)[CH], int lane, int m
         float dmax = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            f[e] = (float)v[c][e] * rcp;
+            // x * RN(1/s) as an FMA with a +0 addend, so the fp16 -> fp32
+            // conversion folds into it (v_fma_mix); it differs from the
+            // product only by giving +0 for -0, which quantizes the same
+            f[e] = __builtin_fmaf((float)v[c][e], rcp, 0.0f);
             q[e] = __builtin_rintf(f[e]);
             dmax = __builtin_fmaxf(dmax, __builtin_fabsf(f[e] - q[e]));
         }
