@@ -24,10 +24,24 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(max(r0, r1), max(r2, r3));
 }
 
+// The sum of the wave's 64 values, wave-uniform: the same DPP steps inside
+// each 16-lane row (a lane and its partner add the same two values, so every
+// lane of a row ends with the same bits), then (r0 + r1) + (r2 + r3) of the
+// four row sums read into scalar registers.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
-    return v;
+    v = dpp_add<0xB1>(v);    // lanes xor 1
+    v = dpp_add<0x4E>(v);    // lanes xor 2
+    v = dpp_add<0x141>(v);   // half-row mirror
+    v = dpp_add<0x140>(v);   // row mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Per-token quantization of one row (a2; aria project page, "Results": W8A8
