@@ -107,9 +107,10 @@ def test_w8a8_prequant_matches_w8a8(q, M, K, N):
 
 
 # the last shape launches 640 workgroups, past the two-per-CU mark where the
-# kernel stops prefetching a block's fragments (both variants are covered)
+# kernel stops prefetching a block's fragments (both variants are covered);
+# 40 and 1000 keys end in a partial key block, 40 in the second of two
 @pytest.mark.parametrize("heads,seq,M", [(1, 1, 1), (1, 64, 64), (2, 100, 200), (3, 130, 130), (2, 257, 514),
-                                         (4, 64, 256), (8, 128, 10240)])
+                                         (4, 64, 256), (8, 128, 10240), (1, 40, 80), (3, 1000, 2000)])
 def test_attention(q, heads, seq, M):
     rng = np.random.default_rng(heads * 1000 + seq)
     W = 64 * heads
