@@ -588,6 +588,8 @@ def main():
                          "(fusion, small_m, m256, ladder, block, step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--steps-per-graph", type=int, default=1,
+                    help="steps captured back to back in one graph (the timed region still runs exactly --steps steps)")
     ap.add_argument("--settle-ms", type=float, default=150.0,
                     help="untimed graph replays after the warm-up, for this long, before timing: the shader "
                          "clock ramps up over the first ~50 steps after an idle period (reported as 'settle')")
@@ -690,6 +692,19 @@ def main():
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
+    graph_n = None
+    spg = max(1, args.steps_per_graph)
+    if graph is not None and spg > 1:
+        # several steps back to back in one graph, as a denoising loop of
+        # `spg` steps replayed as one graph
+        graph_n = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph_n, stream=cap):
+                for _ in range(spg):
+                    step()
+        torch.cuda.current_stream().wait_stream(cap)
+        graph_n.replay()
+        torch.cuda.synchronize()
 
     # untimed settle: replay (or run) the step until `settle_ms` of GPU time
     # have passed, so the timed steps see the clock the step runs at
@@ -710,11 +725,17 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for _ in range(args.steps):
-        if graph is not None:
+    if graph_n is not None:
+        for _ in range(args.steps // spg):
+            graph_n.replay()
+        for _ in range(args.steps % spg):
             graph.replay()
-        else:
-            step()
+    else:
+        for _ in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -852,6 +873,7 @@ def main():
         "timing": ("eager launches" if graph is None else
                    "HIP graph replay of the step" + (" (W8A8 chain and weight-only layers as parallel branches)"
                                                      if concurrent else "")),
+        "steps_per_graph": spg if graph_n is not None else 1,
         "modes": modes,
         "calls": calls,
     }
