@@ -132,6 +132,53 @@ __device__ __forceinline__ void skinny_finish(float (&part)[4][MT * 16][16 * CG 
     __syncthreads();
 }
 
+// The chunk loop with the group scales of each chunk (16 CG rows x KCH / 32
+// groups, contiguous per row) fetched once per workgroup by LDS-DMA, 16 bytes
+// per lane, instead of one 2-byte load per lane and weight load (4-bit
+// weights, K % 256 == 0, so every 16-byte piece of scales lies inside one
+// row).  The same values reach the same MFMAs as with direct loads.
+template <int BITS, int MT, int CG, int NS>
+__device__ __forceinline__ void skinny_chunks_lds_scales(rsrc_t rx, rsrc_t rw, rsrc_t rs, int M, int N, int K, int n0,
+                                                         int wave, int lane, char* sct, v4f (&acc)[MT][CG]) {
+    using RG = SkinnyRegs<BITS, MT, CG, NS>;
+    constexpr int GCH = RG::KCH / 32;             // group scales per row and chunk
+    constexpr int SROW = GCH * 2;                 // their bytes
+    constexpr int SSLOTS = 16 * CG * SROW / 16;   // 16-byte pieces of the tile's scales
+    static_assert(SROW % 16 == 0 && SSLOTS % WAVE == 0, "scale tile in whole waves of 16-byte pieces");
+    const int G = K / 32;
+    const int nkc = (K + RG::KCH - 1) / RG::KCH;
+    for (int kc = 0; kc < nkc; kc++) {
+#pragma unroll
+        for (int r = 0; r < (SSLOTS + 255) / 256; r++) {
+            const int first = r * 256 + wave * WAVE;   // this wave's first slot
+            if (first < SSLOTS) {
+                const int i = first + lane, row = i / (SROW / 16), piece = i % (SROW / 16);
+                const int gi = kc * GCH + piece * 8;
+                const bool ok = i < SSLOTS && n0 + row < N && gi < G;
+                buf_load16_lds(rs, ok ? ((uint32_t)(n0 + row) * (uint32_t)G + (uint32_t)gi) * 2 : OOB, sct + first * 16);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        RG R;
+        skinny_load<BITS, MT, CG, NS, false>(R, rx, rw, rs, M, N, K, n0, kc, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        // the scale pieces went out first: they are in LDS once no more than
+        // this wave's weight and activation loads are outstanding
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(NS * CG + NS * RG::NQ * MT));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NS; j++)
+#pragma unroll
+            for (int c = 0; c < CG; c++) {
+                const int row = 16 * c + lane % 16, gl = (wave * NS + j) * 4 + lane / 16;
+                R.sc[j][c] = *reinterpret_cast<const uint16_t*>(sct + row * SROW + gl * 2);
+            }
+        skinny_compute(R, acc);
+        if (kc + 1 < nkc) __syncthreads();   // before the next chunk's scales overwrite these
+    }
+}
+
 // One linear: a workgroup of 4 waves per 16 CG output channels, one chunk of
 // loads in flight at a time (every load of the chunk issued before any use).
 template <int BITS, int MT, int CG, int NS>
@@ -150,14 +197,25 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const half_t* __restri
     for (int t = 0; t < MT; t++)
 #pragma unroll
         for (int g = 0; g < CG; g++) acc[t][g] = v4f{};
-    const int nkc = (K + RG::KCH - 1) / RG::KCH;
-    for (int kc = 0; kc < nkc; kc++) {
-        RG R;
-        skinny_load(R, rx, rw, rs, M, N, K, n0, kc, wave, lane);
-        // keep the scheduler from sinking loads next to their uses, which
-        // would serialise the chunk into several round trips to memory
-        __builtin_amdgcn_sched_barrier(0);
-        skinny_compute(R, acc);
+    constexpr bool LDS_SCALES = BITS == 4 && (16 * CG * (RG::KCH / 32) * 2 / 16) % WAVE == 0;
+    __shared__ __attribute__((aligned(16))) char sct[LDS_SCALES ? 16 * CG * (RG::KCH / 32) * 2 : 16];
+    bool done = false;
+    if constexpr (LDS_SCALES) {
+        if (K % 256 == 0) {
+            skinny_chunks_lds_scales<BITS, MT, CG, NS>(rx, rw, rs, M, N, K, n0, wave, lane, sct, acc);
+            done = true;
+        }
+    }
+    if (!done) {
+        const int nkc = (K + RG::KCH - 1) / RG::KCH;
+        for (int kc = 0; kc < nkc; kc++) {
+            RG R;
+            skinny_load(R, rx, rw, rs, M, N, K, n0, kc, wave, lane);
+            // keep the scheduler from sinking loads next to their uses, which
+            // would serialise the chunk into several round trips to memory
+            __builtin_amdgcn_sched_barrier(0);
+            skinny_compute(R, acc);
+        }
     }
     skinny_finish<BITS, MT, CG>(part, acc, S, Y, M, N, epi, n0, wave, lane);
 }
@@ -197,37 +255,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_grouped_kernel(SkinnyGroup g)
         for (int c = 0; c < CG; c++) acc[t][c] = v4f{};
     const int nkc = (P.K + RG::KCH - 1) / RG::KCH;
     if (BITS == 4 && P.K % 256 == 0) {
-        // G % 8 == 0: every 16-byte piece of scales lies inside one row
-        for (int kc = 0; kc < nkc; kc++) {
-#pragma unroll
-            for (int r = 0; r < (SSLOTS + 255) / 256; r++) {
-                const int first = r * 256 + wave * WAVE;   // this wave's first slot
-                if (first < SSLOTS) {
-                    const int i = first + lane, row = i / (SROW / 16), piece = i % (SROW / 16);
-                    const int gi = kc * GCH + piece * 8;
-                    const bool ok = i < SSLOTS && n0 + row < P.N && gi < G;
-                    buf_load16_lds(rs, ok ? ((uint32_t)(n0 + row) * (uint32_t)G + (uint32_t)gi) * 2 : OOB, sct + first * 16);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            RG R;
-            skinny_load<BITS, MT, CG, NS, false>(R, rx, rw, rs, P.M, P.N, P.K, n0, kc, wave, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            // the scale pieces went out first: they are in LDS once no more than
-            // this wave's weight and activation loads are outstanding
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(NS * CG + NS * RG::NQ * MT));
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < NS; j++)
-#pragma unroll
-                for (int c = 0; c < CG; c++) {
-                    const int row = 16 * c + lane % 16, gl = (wave * NS + j) * 4 + lane / 16;
-                    R.sc[j][c] = *reinterpret_cast<const uint16_t*>(sct + row * SROW + gl * 2);
-                }
-            skinny_compute(R, acc);
-            if (kc + 1 < nkc) __syncthreads();   // before the next chunk's scales overwrite these
-        }
+        skinny_chunks_lds_scales<BITS, MT, CG, NS>(rx, rw, rs, P.M, P.N, P.K, n0, wave, lane, sct, acc);
     } else {
         for (int kc = 0; kc < nkc; kc++) {
             RG R;
