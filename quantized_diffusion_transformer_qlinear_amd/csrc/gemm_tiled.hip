@@ -655,7 +655,15 @@ constexpr TileCfg kTiles[] = {
     // tile, K = 2048: W8A8 22.6 -> 20.8 us, W8A16 23.5 -> 22.2, W4A16 26.2 ->
     // 25.0; K = 8192: W8A8 the same, W8A16 / W4A16 slower than the two-group
     // 4-wave tile, which keeps the higher price for those modes
-    {128, 128, 2, 4, 1, {2926.f, 2002.f, 1650.f, 1880.f}}};
+    {128, 128, 2, 4, 1, {2926.f, 2002.f, 1650.f, 1880.f}},
+    // the 6-wave 64x96 tile with two K groups (12 waves, one workgroup per
+    // CU) for mid-size M, where a tile's K-loop is a latency chain: halving
+    // the chain paid for the weight-only modes, measured against the picks
+    // before it (interleaved graph replays, two runs): W8A16 M = 256,
+    // 1536 -> 6144 11.9 -> 10.8 us, 8192 -> 2048 39.5 -> 35.4 us; W4A16
+    // 8192 -> 2048 43.7 -> 38.8 us, M = 192, 1536 -> 4608 12.3 -> 10.8 us,
+    // within +-4 % at M = 128 and 256, 1536 -> 6144; W8A8 slower everywhere
+    {64, 96, 2, 3, 2, {1000.f, 1800.f, 1500.f, 1000.f}}};
 
 int num_cus() {
     static int cus = 0;
@@ -723,7 +731,7 @@ hipError_t launch_mode(const TileCfg& t, const void* a, const uint8_t* b, const 
     ARIA_TILE(128, 256, 2, 4, 1) ARIA_TILE(128, 192, 2, 2, 1) ARIA_TILE(128, 128, 2, 2, 1) ARIA_TILE(64, 192, 2, 2, 1)
     ARIA_TILE(128, 64, 2, 2, 1) ARIA_TILE(64, 128, 2, 2, 1) ARIA_TILE(64, 64, 2, 2, 1)
     ARIA_TILE(64, 192, 2, 2, 2) ARIA_TILE(128, 128, 2, 2, 2) ARIA_TILE(128, 64, 2, 2, 2) ARIA_TILE(64, 128, 2, 2, 2)
-    ARIA_TILE(64, 96, 2, 3, 1) ARIA_TILE(128, 96, 2, 3, 1) ARIA_TILE(128, 128, 2, 4, 1)
+    ARIA_TILE(64, 96, 2, 3, 1) ARIA_TILE(128, 96, 2, 3, 1) ARIA_TILE(128, 128, 2, 4, 1) ARIA_TILE(64, 96, 2, 3, 2)
 #undef ARIA_TILE
     return hipErrorInvalidValue;
 }
