@@ -10,8 +10,8 @@
 //   W16A16: acc = sum_k X[m][k] * Wt[n][k]  (fp32);  y = acc
 // then y -> + bias -> GELU -> + residual -> + alpha d -> fp16.
 //
-// Design (gfx950): a workgroup of WM x WN waves (4, 6, 8, 12 or 16; a 4-wave tile
-// may also run as two such groups that split the K-steps) owns a BM x BN
+// Design (gfx950): a workgroup of WM x WN waves (4, 6, 8, 12 or 16; a 4- or
+// 6-wave tile may also run as two such groups that split the K-steps) owns a BM x BN
 // output tile; each wave owns (BM/WM) x (BN/WN) as 32x32 blocks on the matrix cores
 // (v_mfma_i32_32x32x32_i8 or v_mfma_f32_32x32x16_f16).  Both operands live in
 // LDS as rows of 128 bytes (128 int8 k or 64 fp16 k) plus a 16-byte pad that
