@@ -104,6 +104,23 @@ def test_actquant_ragged(q, M, K):
     _actquant_both(q, x)
 
 
+@pytest.mark.parametrize("K", [64, 1536, 6144])
+def test_actquant_max_in_every_lane(q, K):
+    """Row m holds its largest magnitude in the k that lane m % 64 of the
+    row's wave loads (element c * 512 + lane * 8 + e): the wave-wide maximum
+    must reach every lane, whichever 16-lane row of the wave it starts in.
+    Signs alternate so that a reduction over signed values would also fail."""
+    rng = np.random.default_rng(K)
+    M = 128
+    x = (rng.standard_normal((M, K)) * 0.5).astype(np.float16)
+    for m in range(M):
+        lane, c, e = m % 64, (m // 64) % max(1, K // 512), m % 8
+        k = min(c * 512 + lane * 8 + e, K - 1)
+        x[m, k] = np.float16((-1) ** m * (8.0 + m / 16))
+    log(f"actquant max in every lane K={K}")
+    _actquant_both(q, x)
+
+
 def test_actquant_fp16_grid(q):
     """Every finite fp16 value is quantized under scales with ties, subnormal
     scales and the largest input."""
